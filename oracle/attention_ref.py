@@ -1,0 +1,375 @@
+"""Plain fp64 CPU oracle for exact attention, forward and backward.
+
+TEST INFRASTRUCTURE ONLY. This module is the checker that the HIP library is
+compared against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it; the library itself never
+does, and this module imports nothing from the library.
+
+Everything here is written for a reader who has the pages open and wants to
+check the arithmetic by eye: no blocking, fusion or reordering beyond what the
+cited definition or algorithm states.  Arrays are numpy float64; a problem is
+one attention head with Q, K, V of shape [N, d].  Batched helpers loop over
+leading (batch, head) axes one head at a time.
+
+Sources (page title -> part used):
+
+* "Overview of Flash Attention series", section *Standard Attention
+  Implementation / Forward Pass*: S = Q K^T, P = softmax(S) row-wise, O = P V.
+* "Transformer 入门" (Transformer primer), *flash attention* definitions:
+  S = Q K^T / sqrt(d), m = rowmax(S), l = rowsum(exp(S - m)), and the
+  safe-softmax one-liner.
+* "FlashAttention in NeurIPS 2022" (coreui blog), section 2.1 *拆分*
+  (splitting): the max-shifted softmax, the block-wise update of m and l, and
+  the normalised update of the output vector o.
+* "Overview of Flash Attention series", section *Tiling* (the two-block
+  decomposition of m, f, l) and *Analysis / Correctness*, Theorem 1 (the
+  invariants after each K/V block).
+* "Как работает FlashAttention математически" (How FlashAttention works
+  mathematically), sections 3-4 (online softmax; the running output kept
+  un-normalised and divided once at the end) and section 6 (the per-Q-block
+  loop).
+* "Overview of Flash Attention series", section *Backward Pass of
+  flashattention*: dV = P^T dO, dP = dO V^T, D_i = P_i:^T dP_i: = do_i^T o_i,
+  dS = P o (dP - D), dq_i = sum_j dS_ij k_j, dk_j = sum_i dS_ij q_i.
+
+Readings taken where the pages are silent or disagree (each one is listed in
+the design notes of the repository):
+
+* The scale factor is an explicit argument applied to S before the softmax;
+  the default is 1/sqrt(d) as in the primer's definitions.  Because
+  S = scale * Q K^T, the chain rule puts a factor ``scale`` on dQ and dK.
+* The causal mask keeps key index <= query index; masked scores are -inf
+  (zero weight after the softmax), not 0.
+* The stored row statistic is lse_i = m_i + ln l_i = ln sum_j exp(S_ij) over
+  the unmasked j, natural log, of the *scaled* scores.
+* In the coreui worked example the split is along keys (what the primer calls
+  T_c / B_c); a block holds keys [j*Bc, (j+1)*Bc), end exclusive.
+
+Parity status: every public function here is pinned by tests/test_oracle.py
+(page worked example, closed forms, library cross-checks, brute force,
+finite differences); none is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Tuple
+
+import numpy as np
+
+__all__ = [
+    "default_scale",
+    "scores",
+    "softmax_stats",
+    "forward_head",
+    "forward",
+    "forward_rows",
+    "backward_head",
+    "backward",
+    "online_softmax_blocks",
+    "blockwise_forward_head",
+    "brute_force_forward_head",
+    "finite_difference_grads",
+]
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d): the primer's definition S = Q K^T / sqrt(d)."""
+    return 1.0 / math.sqrt(d)
+
+
+def _as_f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool) -> np.ndarray:
+    """S = scale * Q K^T for one head, with S[r, c] = -inf where c > r if causal.
+
+    Standard attention, forward pass ("Overview of Flash Attention series");
+    the scale as in the primer's definitions.  q: [Nq, d], k: [Nk, d].
+    """
+    s = scale * (_as_f64(q) @ _as_f64(k).T)
+    if causal:
+        nq, nk = s.shape
+        rows = np.arange(nq)[:, None]
+        cols = np.arange(nk)[None, :]
+        s = np.where(cols > rows, -np.inf, s)
+    return s
+
+
+def softmax_stats(s: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Row-wise safe softmax of a score matrix: returns (P, m, l).
+
+    m = rowmax(S), f = exp(S - m), l = rowsum(f), P = f / l
+    (coreui blog section 2.1; primer definitions of m and l).
+    """
+    m = np.max(s, axis=-1)
+    f = np.exp(s - m[..., None])
+    l = np.sum(f, axis=-1)
+    p = f / l[..., None]
+    return p, m, l
+
+
+def forward_head(q, k, v, causal: bool = False, scale: Optional[float] = None):
+    """Standard attention for one head: returns (O, lse).
+
+    S = scale Q K^T (masked if causal), P = softmax(S), O = P V,
+    lse = m + ln l.  Materialises the N x N matrices S and P, which is
+    exactly what the tiled method avoids; this is the definition it must
+    reproduce (Theorem 1, "Overview of Flash Attention series").
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    s = scores(q, k, scale, causal)
+    p, m, l = softmax_stats(s)
+    o = p @ v
+    lse = m + np.log(l)
+    return o, lse
+
+
+def _loop_heads(fn, arrays, *args):
+    """Apply a one-head function over the leading axes of [..., N, d] arrays."""
+    lead = arrays[0].shape[:-2]
+    outs = None
+    for idx in np.ndindex(*lead):
+        res = fn(*[a[idx] for a in arrays], *args)
+        if outs is None:
+            outs = [np.empty(lead + r.shape, dtype=np.float64) for r in res]
+        for o, r in zip(outs, res):
+            o[idx] = r
+    return tuple(outs)
+
+
+def forward(q, k, v, causal: bool = False, scale: Optional[float] = None):
+    """Standard attention over [..., N, d] inputs, one head at a time."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    return _loop_heads(forward_head, (q, k, v), causal, scale)
+
+
+def forward_rows(q, k, v, rows, causal: bool = False, scale: Optional[float] = None):
+    """Standard attention restricted to the query rows ``rows`` of one head.
+
+    The same definition as :func:`forward_head`, evaluated only for the listed
+    query indices (each output row depends on its own query row and on all of
+    K and V, with the causal mask taken at the row's own index).  Used to
+    check sampled outputs of full-size problems.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    rows = np.asarray(rows, dtype=np.int64)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    s = scale * (q[rows] @ k.T)
+    if causal:
+        cols = np.arange(k.shape[0])[None, :]
+        s = np.where(cols > rows[:, None], -np.inf, s)
+    p, m, l = softmax_stats(s)
+    return p @ v, m + np.log(l)
+
+
+def backward_head(q, k, v, do, causal: bool = False, scale: Optional[float] = None):
+    """Naive chain-rule backward of standard attention for one head.
+
+    With S = scale Q K^T, P = softmax(S), O = P V and upstream gradient dO
+    ("Overview of Flash Attention series", Backward Pass):
+      dV = P^T dO
+      dP = dO V^T
+      D_i = P_i:^T dP_i:            (the row term of the softmax Jacobian)
+      dS = P o (dP - D)            (elementwise, D broadcast along rows)
+      dQ = scale * dS K            (dq_i = sum_j dS_ij k_j, times scale)
+      dK = scale * dS^T Q          (dk_j = sum_i dS_ij q_i, times scale)
+    Returns (dQ, dK, dV).
+    """
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    s = scores(q, k, scale, causal)
+    p, _, _ = softmax_stats(s)
+    dv = p.T @ do
+    dp = do @ v.T
+    dsum = np.sum(p * dp, axis=-1)
+    ds = p * (dp - dsum[:, None])
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def backward(q, k, v, do, causal: bool = False, scale: Optional[float] = None):
+    """Chain-rule backward over [..., N, d] inputs, one head at a time."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    return _loop_heads(backward_head, (q, k, v, do), causal, scale)
+
+
+def online_softmax_blocks(s_row, v, block: int):
+    """The coreui blog's block-by-block softmax of one score row, with output.
+
+    Section 2.1 of "FlashAttention in NeurIPS 2022": start from m = -inf,
+    l = 0, o = 0; for each key block i with local max m_i, numerator vector
+    p_i = exp(s_block - m_i) and local sum l_i:
+      m_new = max(m, m_i)
+      l_new = exp(m - m_new) * l + exp(m_i - m_new) * l_i
+      o_new = (l * exp(m - m_new) * o + exp(m_i - m_new) * p_i V_i) / l_new
+    Returns the list of (m, l, o) after each block.
+    """
+    s_row = _as_f64(s_row)
+    v = _as_f64(v)
+    m = -np.inf
+    l = 0.0
+    o = np.zeros(v.shape[1], dtype=np.float64)
+    history = []
+    for start in range(0, s_row.shape[0], block):
+        blk = s_row[start:start + block]
+        m_i = np.max(blk)
+        p_i = np.exp(blk - m_i)
+        l_i = np.sum(p_i)
+        m_new = max(m, m_i)
+        a_old = math.exp(m - m_new) if m > -np.inf else 0.0
+        a_new = math.exp(m_i - m_new)
+        l_new = a_old * l + a_new * l_i
+        o = (l * a_old * o + a_new * (p_i @ v[start:start + block])) / l_new
+        m, l = m_new, l_new
+        history.append((m, l, o.copy()))
+    return history
+
+
+def blockwise_forward_head(q, k, v, block_q: int, block_k: int, causal: bool = False,
+                           scale: Optional[float] = None, form: str = "deferred",
+                           check_invariants: bool = False):
+    """Tiled forward for one head in the pages' loop order: returns (O, lse).
+
+    Q is cut into blocks of ``block_q`` rows and K, V into blocks of
+    ``block_k`` rows (primer: T_r = ceil(N/B_r), T_c = ceil(N/B_c)).  For
+    each Q block (the primer's "V2" order: Q outer, K/V inner; the result
+    does not depend on the order) the running m, l, O start at -inf, 0, 0
+    and each K/V block updates them by the online-softmax rule:
+      m_new = max(m, rowmax(S_ij))
+      l_new = exp(m - m_new) l + rowsum(exp(S_ij - m_new))
+    and the output either
+
+    * ``form="normalised"``: O = (l/l_new) exp(m - m_new) O
+      + (1/l_new) exp(S_ij - m_new) V_j   (section 6 of the aivaro page,
+      the coreui o-update), or
+    * ``form="deferred"``: O = exp(m - m_new) O + exp(S_ij - m_new) V_j and a
+      single division by l after the last block (section 4 of the aivaro
+      page: kept un-normalised, normalised once at the end).
+
+    With ``check_invariants`` the Theorem 1 invariants ("Overview of Flash
+    Attention series", Correctness) are asserted after each K/V block:
+    m = rowmax of the scores seen so far, l = rowsum(exp(S_seen - m)),
+    normalised O = softmax(S_seen) V_seen.  A row with no unmasked key yet
+    keeps m = -inf, l = 0, O = 0 (the -inf - (-inf) case is taken as weight 0).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    if form not in ("deferred", "normalised"):
+        raise ValueError(form)
+    n_q, d = q.shape
+    n_k = k.shape[0]
+    if scale is None:
+        scale = default_scale(d)
+    o_all = np.zeros((n_q, v.shape[1]))
+    lse_all = np.zeros(n_q)
+    s_full = scores(q, k, scale, causal) if check_invariants else None
+    for qs in range(0, n_q, block_q):
+        rows = np.arange(qs, min(qs + block_q, n_q))
+        q_i = q[rows]
+        m = np.full(rows.size, -np.inf)
+        l = np.zeros(rows.size)
+        o = np.zeros((rows.size, v.shape[1]))
+        for ks in range(0, n_k, block_k):
+            cols = np.arange(ks, min(ks + block_k, n_k))
+            s_ij = scale * (q_i @ k[cols].T)
+            if causal:
+                s_ij = np.where(cols[None, :] > rows[:, None], -np.inf, s_ij)
+            m_new = np.maximum(m, np.max(s_ij, axis=1))
+            # weight 0 for rows that have seen no unmasked key yet
+            safe = np.where(np.isfinite(m_new), m_new, 0.0)
+            alpha = np.where(np.isfinite(m), np.exp(m - safe), 0.0)
+            p_ij = np.exp(s_ij - safe[:, None])
+            l_new = alpha * l + np.sum(p_ij, axis=1)
+            if form == "normalised":
+                with np.errstate(invalid="ignore", divide="ignore"):
+                    inv = np.where(l_new > 0, 1.0 / l_new, 0.0)
+                o = (l * inv * alpha)[:, None] * o + inv[:, None] * (p_ij @ v[cols])
+            else:
+                o = alpha[:, None] * o + p_ij @ v[cols]
+            m, l = m_new, l_new
+            if check_invariants:
+                seen = s_full[rows][:, :cols[-1] + 1]
+                ref_m = np.max(seen, axis=1)
+                assert np.array_equal(np.isfinite(ref_m), np.isfinite(m))
+                fin = np.isfinite(ref_m)
+                np.testing.assert_allclose(m[fin], ref_m[fin], rtol=0, atol=1e-12)
+                ref_l = np.sum(np.exp(seen[fin] - ref_m[fin][:, None]), axis=1)
+                np.testing.assert_allclose(l[fin], ref_l, rtol=1e-12, atol=0)
+                ref_o = (np.exp(seen[fin] - ref_m[fin][:, None]) / ref_l[:, None]) @ v[:cols[-1] + 1]
+                got_o = o[fin] if form == "normalised" else o[fin] / l[fin][:, None]
+                np.testing.assert_allclose(got_o, ref_o, rtol=1e-12, atol=1e-12)
+        if form == "deferred":
+            o = o / l[:, None]
+        o_all[rows] = o
+        lse_all[rows] = m + np.log(l)
+    return o_all, lse_all
+
+
+def brute_force_forward_head(q, k, v, causal: bool = False, scale: Optional[float] = None):
+    """Attention by scalar loops with math.exp, for tiny problems only.
+
+    Each output row o_i = sum_j exp(s_ij) v_j / sum_j exp(s_ij) with
+    s_ij = scale * sum_c q_ic k_jc ("Overview of Flash Attention series",
+    Forward Pass of flashattention: the normaliser L_i and o_i written per
+    row), evaluated with a max shift for range.  No numpy arithmetic, so it
+    shares no code path with :func:`forward_head`.
+    """
+    q = [[float(x) for x in row] for row in np.asarray(q)]
+    k = [[float(x) for x in row] for row in np.asarray(k)]
+    v = [[float(x) for x in row] for row in np.asarray(v)]
+    n_q, d = len(q), len(q[0])
+    dv = len(v[0])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o_rows: List[List[float]] = []
+    lse_rows: List[float] = []
+    for i in range(n_q):
+        keys = [j for j in range(len(k)) if not (causal and j > i)]
+        s = [scale * math.fsum(q[i][c] * k[j][c] for c in range(d)) for j in keys]
+        mx = max(s)
+        w = [math.exp(x - mx) for x in s]
+        tot = math.fsum(w)
+        o_rows.append([math.fsum(w[t] * v[j][c] for t, j in enumerate(keys)) / tot for c in range(dv)])
+        lse_rows.append(mx + math.log(tot))
+    return np.array(o_rows), np.array(lse_rows)
+
+
+def finite_difference_grads(q, k, v, g, causal: bool = False, scale: Optional[float] = None,
+                            h: float = 1e-6):
+    """Central differences of phi(Q, K, V) = sum(O * G) for one head.
+
+    The gradient of phi with respect to O is G, so these are the dQ, dK, dV
+    that the backward must return for dO = G.  Every element is perturbed by
+    +-h in turn; tiny problems only.
+    """
+    q, k, v, g = _as_f64(q).copy(), _as_f64(k).copy(), _as_f64(v).copy(), _as_f64(g)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+
+    def phi():
+        o, _ = forward_head(q, k, v, causal, scale)
+        return float(np.sum(o * g))
+
+    grads = []
+    for x in (q, k, v):
+        gx = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            keep = x[idx]
+            x[idx] = keep + h
+            up = phi()
+            x[idx] = keep - h
+            dn = phi()
+            x[idx] = keep
+            gx[idx] = (up - dn) / (2.0 * h)
+        grads.append(gx)
+    return tuple(grads)

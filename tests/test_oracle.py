@@ -1,0 +1,356 @@
+"""Pins for the fp64 oracle: it is checked against things other than itself.
+
+* the coreui blog's worked example (section 2.1), stored under tests/golden/
+  in the page's own notation and evaluated here with math.exp;
+* closed forms (N = 1, K = 0, scale = 0, constant V, causal row 0);
+* independent library routines (torch's float64 scaled_dot_product_attention
+  and autograd, scipy's logsumexp);
+* brute force by scalar loops on tiny inputs;
+* central finite differences for the backward;
+* invariants the pages state (rows of P sum to 1, block-wise recurrence equals
+  the one-shot softmax, Theorem 1's per-block invariants, D_i = do_i . o_i).
+
+All CPU-only.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import attention_ref as ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example_softmax.json")
+
+
+def _rand(shape, seed, mult=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * mult
+
+
+def _page_sum(terms):
+    return math.fsum(math.exp(a - b) for a, b in terms)
+
+
+@pytest.fixture(scope="module")
+def worked():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- worked example
+
+def test_worked_example_block_history(worked):
+    s = np.array(worked["scores"], dtype=np.float64)
+    v = np.array(worked["V"], dtype=np.float64)
+    hist = ref.online_softmax_blocks(s, v, worked["block"])
+    assert len(hist) == len(worked["after_block"])
+    for (m, l, o), page in zip(hist, worked["after_block"]):
+        assert m == page["m"]
+        assert l == pytest.approx(_page_sum(page["l"]), rel=1e-15)
+        num = np.zeros(2)
+        for a, b, r in page["o_numerator"]:
+            num += math.exp(a - b) * v[r]
+        o_page = num / _page_sum(page["o_denominator"])
+        np.testing.assert_allclose(o, o_page, rtol=1e-14, atol=0)
+
+
+def test_worked_example_final_equals_softmax_times_v(worked):
+    s = np.array(worked["scores"], dtype=np.float64)
+    v = np.array(worked["V"], dtype=np.float64)
+    den = _page_sum(worked["softmax_shifted_denominator"])
+    p_page = np.array([math.exp(a - b) for a, b in worked["softmax_shifted_numerators"]]) / den
+    # unshifted form as first printed on the page: e^{s_j} / sum_k e^{s_k}
+    p_plain = np.array([math.exp(x) for x in s]) / math.fsum(math.exp(x) for x in s)
+    np.testing.assert_allclose(p_page, p_plain, rtol=1e-14)
+    m, l, o = ref.online_softmax_blocks(s, v, worked["block"])[-1]
+    np.testing.assert_allclose(o, p_page @ v, rtol=1e-14)
+    # the final l equals the one-shot shifted denominator
+    assert l == pytest.approx(den, rel=1e-15)
+    assert m == max(worked["scores"])
+
+
+@pytest.mark.parametrize("form", ["deferred", "normalised"])
+def test_worked_example_as_attention_problem(worked, form):
+    """q = [1], k_j = [s_j], scale 1 reproduces the page's score row."""
+    s = np.array(worked["scores"], dtype=np.float64)
+    v = np.array(worked["V"], dtype=np.float64)
+    q = np.ones((1, 1))
+    k = s[:, None]
+    den = _page_sum(worked["softmax_shifted_denominator"])
+    num = sum(math.exp(a - b) * v[r] for (a, b), r in zip(worked["softmax_shifted_numerators"], range(4)))
+    o_page = num / den
+    lse_page = 10.0 + math.log(den)
+    o, lse = ref.blockwise_forward_head(q, k, v, 1, worked["block"], scale=1.0, form=form,
+                                        check_invariants=True)
+    np.testing.assert_allclose(o[0], o_page, rtol=1e-14)
+    assert lse[0] == pytest.approx(lse_page, rel=1e-15)
+    o1, lse1 = ref.forward_head(q, k, v, scale=1.0)
+    np.testing.assert_allclose(o1[0], o_page, rtol=1e-14)
+    assert lse1[0] == pytest.approx(lse_page, rel=1e-15)
+
+
+# ---------------------------------------------------------------- forward pins
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,d", [(1, 1), (2, 2), (3, 4), (5, 3), (8, 8)])
+def test_forward_matches_brute_force(n, d, causal):
+    q, k, v = _rand((n, d), 1), _rand((n, d), 2), _rand((n, d + 1), 3)
+    o, lse = ref.forward_head(q, k, v, causal=causal, scale=0.7)
+    o_b, lse_b = ref.brute_force_forward_head(q, k, v, causal=causal, scale=0.7)
+    np.testing.assert_allclose(o, o_b, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_b, rtol=0, atol=1e-12)
+
+
+def test_forward_rectangular_brute_force():
+    q, k, v = _rand((3, 4), 4), _rand((7, 4), 5), _rand((7, 2), 6)
+    o, lse = ref.forward_head(q, k, v, scale=0.3)
+    o_b, lse_b = ref.brute_force_forward_head(q, k, v, scale=0.3)
+    np.testing.assert_allclose(o, o_b, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_b, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("scale", [None, 0.05, 1.3])
+def test_forward_matches_torch_sdpa_float64(causal, scale):
+    b, h, n, d = 2, 3, 67, 16
+    q, k, v = _rand((b, h, n, d), 7), _rand((b, h, n, d), 8), _rand((b, h, n, d), 9)
+    o, lse = ref.forward(q, k, v, causal=causal, scale=scale)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    o_t = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    np.testing.assert_allclose(o, o_t.numpy(), rtol=0, atol=1e-12)
+    sc = ref.default_scale(d) if scale is None else scale
+    s = sc * np.einsum("bhid,bhjd->bhij", q, k)
+    if causal:
+        s = np.where(np.triu(np.ones((n, n), bool), 1), -np.inf, s)
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(s, axis=-1), rtol=0, atol=1e-12)
+
+
+def test_forward_rows_equals_full_rows():
+    q, k, v = _rand((50, 8), 10), _rand((50, 8), 11), _rand((50, 8), 12)
+    rows = [0, 3, 17, 49]
+    for causal in (False, True):
+        o, lse = ref.forward_head(q, k, v, causal=causal)
+        o_r, lse_r = ref.forward_rows(q, k, v, rows, causal=causal)
+        np.testing.assert_allclose(o_r, o[rows], atol=1e-13)
+        np.testing.assert_allclose(lse_r, lse[rows], atol=1e-13)
+
+
+def test_closed_form_single_key():
+    q, k, v = _rand((1, 6), 13), _rand((1, 6), 14), _rand((1, 6), 15)
+    o, lse = ref.forward_head(q, k, v, scale=0.4)
+    np.testing.assert_allclose(o, v, rtol=0, atol=0)
+    assert lse[0] == pytest.approx(0.4 * float(q[0] @ k[0]), rel=1e-15)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_closed_form_zero_keys_and_zero_scale(causal):
+    n, d = 9, 5
+    q, v = _rand((n, d), 16), _rand((n, d), 17)
+    allowed = np.arange(1, n + 1) if causal else np.full(n, n)
+    means = np.array([v[: allowed[r]].mean(axis=0) for r in range(n)])
+    o, lse = ref.forward_head(q, np.zeros((n, d)), v, causal=causal)
+    np.testing.assert_allclose(o, means, atol=1e-14)
+    np.testing.assert_allclose(lse, np.log(allowed), atol=1e-14)
+    o0, lse0 = ref.forward_head(q, _rand((n, d), 18), v, causal=causal, scale=0.0)
+    np.testing.assert_allclose(o0, means, atol=1e-14)
+    np.testing.assert_allclose(lse0, np.log(allowed), atol=1e-14)
+
+
+def test_closed_form_constant_values_and_causal_first_row():
+    n, d = 12, 4
+    q, k = _rand((n, d), 19), _rand((n, d), 20)
+    o, _ = ref.forward_head(q, k, np.full((n, d), 2.5))
+    np.testing.assert_allclose(o, 2.5, atol=1e-14)
+    v = _rand((n, d), 21)
+    o, lse = ref.forward_head(q, k, v, causal=True, scale=0.9)
+    np.testing.assert_allclose(o[0], v[0], atol=0)
+    assert lse[0] == pytest.approx(0.9 * float(q[0] @ k[0]), rel=1e-15)
+
+
+def test_rows_of_p_sum_to_one_and_mask_is_exact_zero():
+    q, k = _rand((40, 8), 22), _rand((40, 8), 23)
+    s = ref.scores(q, k, 0.5, causal=True)
+    p, m, l = ref.softmax_stats(s)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-13)
+    assert np.all(p[np.triu(np.ones((40, 40), bool), 1)] == 0.0)
+    assert np.all(p >= 0)
+
+
+def test_softmax_shift_invariance():
+    s = _rand((5, 11), 24, 3.0)
+    p, _, _ = ref.softmax_stats(s)
+    p2, _, _ = ref.softmax_stats(s + _rand((5, 1), 25, 50.0))
+    np.testing.assert_allclose(p, p2, atol=1e-14)
+    np.testing.assert_allclose(p, scipy.special.softmax(s, axis=1), atol=1e-15)
+
+
+def test_causal_prefix_property():
+    n, d = 30, 6
+    q, k, v = _rand((n, d), 26), _rand((n, d), 27), _rand((n, d), 28)
+    o, lse = ref.forward_head(q, k, v, causal=True)
+    r = 11
+    k2, v2 = k.copy(), v.copy()
+    k2[r + 1:] += 5.0
+    v2[r + 1:] -= 3.0
+    o2, lse2 = ref.forward_head(q, k2, v2, causal=True)
+    np.testing.assert_array_equal(o2[: r + 1], o[: r + 1])
+    np.testing.assert_array_equal(lse2[: r + 1], lse[: r + 1])
+    assert not np.allclose(o2[r + 1:], o[r + 1:])
+
+
+@pytest.mark.parametrize("form", ["deferred", "normalised"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bq,bk", [(1, 1), (5, 2), (16, 3), (7, 7), (64, 64), (33, 65)])
+def test_blockwise_equals_one_shot(form, causal, bq, bk):
+    n, d = 65, 8
+    q, k, v = _rand((n, d), 29, 2.0), _rand((n, d), 30, 2.0), _rand((n, d), 31)
+    o, lse = ref.forward_head(q, k, v, causal=causal)
+    ob, lseb = ref.blockwise_forward_head(q, k, v, bq, bk, causal=causal, form=form,
+                                          check_invariants=(bq * bk <= 256))
+    np.testing.assert_allclose(ob, o, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lseb, lse, rtol=1e-12, atol=1e-12)
+
+
+def test_blockwise_with_large_key_outliers():
+    """Later key blocks raise the running max many times (rescaling path)."""
+    n, d = 96, 16
+    q, k, v = _rand((n, d), 32, 0.5), _rand((n, d), 33, 0.5), _rand((n, d), 34, 0.5)
+    k[np.arange(5, n, 17)] *= 40.0
+    o, lse = ref.forward_head(q, k, v, causal=True)
+    for form in ("deferred", "normalised"):
+        ob, lseb = ref.blockwise_forward_head(q, k, v, 32, 8, causal=True, form=form,
+                                              check_invariants=True)
+        np.testing.assert_allclose(ob, o, rtol=1e-11, atol=1e-11)
+        np.testing.assert_allclose(lseb, lse, rtol=1e-12, atol=1e-11)
+
+
+def test_batched_forward_equals_per_head():
+    q, k, v = _rand((2, 2, 9, 4), 35), _rand((2, 2, 9, 4), 36), _rand((2, 2, 9, 4), 37)
+    o, lse = ref.forward(q, k, v, causal=True)
+    for b in range(2):
+        for h in range(2):
+            o1, l1 = ref.forward_head(q[b, h], k[b, h], v[b, h], causal=True)
+            np.testing.assert_array_equal(o[b, h], o1)
+            np.testing.assert_array_equal(lse[b, h], l1)
+
+
+# ---------------------------------------------------------------- backward pins
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,d", [(1, 1), (2, 2), (3, 4), (5, 2), (8, 4)])
+def test_backward_matches_finite_differences(n, d, causal):
+    q, k, v, g = (_rand((n, d), s) for s in (40, 41, 42, 43))
+    dq, dk, dv = ref.backward_head(q, k, v, g, causal=causal, scale=0.8)
+    fq, fk, fv = ref.finite_difference_grads(q, k, v, g, causal=causal, scale=0.8)
+    np.testing.assert_allclose(dq, fq, rtol=0, atol=1e-7)
+    np.testing.assert_allclose(dk, fk, rtol=0, atol=1e-7)
+    np.testing.assert_allclose(dv, fv, rtol=0, atol=1e-7)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_torch_autograd_float64(causal):
+    b, h, n, d = 2, 2, 45, 8
+    q, k, v, do = (_rand((b, h, n, d), s) for s in (44, 45, 46, 47))
+    dq, dk, dv = ref.backward(q, k, v, do, causal=causal, scale=0.6)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.6)
+    o.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+def test_d_identity_and_gradient_invariants():
+    """D_i = P_i:^T dP_i: = do_i . o_i, and two sums fixed by the softmax."""
+    n, d = 33, 8
+    q, k, v, do = (_rand((n, d), s) for s in (48, 49, 50, 51))
+    for causal in (False, True):
+        s = ref.scores(q, k, 0.35, causal)
+        p, _, _ = ref.softmax_stats(s)
+        o, _ = ref.forward_head(q, k, v, causal=causal, scale=0.35)
+        dp = do @ v.T
+        np.testing.assert_allclose((p * dp).sum(axis=1), (do * o).sum(axis=1), atol=1e-12)
+        dq, dk, dv = ref.backward_head(q, k, v, do, causal=causal, scale=0.35)
+        # shifting every key by the same vector adds a per-row constant to S:
+        # O is unchanged, so the key gradients sum to zero
+        np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
+        # shifting every value row by c shifts every output row by c
+        np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), atol=1e-12)
+
+
+def test_backward_single_key_closed_form():
+    q, k, v, do = (_rand((1, 5), s) for s in (52, 53, 54, 55))
+    dq, dk, dv = ref.backward_head(q, k, v, do)
+    np.testing.assert_allclose(dv, do, atol=0)
+    np.testing.assert_allclose(dq, 0.0, atol=0)
+    np.testing.assert_allclose(dk, 0.0, atol=0)
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _fd_pin(backward_fn):
+    n, d = 4, 3
+    q, k, v, g = (_rand((n, d), s) for s in (60, 61, 62, 63))
+    got = backward_fn(q, k, v, g, True, 0.8)
+    want = ref.finite_difference_grads(q, k, v, g, causal=True, scale=0.8)
+    return all(np.allclose(a, b, atol=1e-7) for a, b in zip(got, want))
+
+
+def test_pins_catch_planted_backward_mistakes():
+    """Each plausible slip in the chain rule fails the finite-difference pin."""
+    assert _fd_pin(ref.backward_head)
+
+    def no_scale_on_dq(q, k, v, do, causal, scale):
+        dq, dk, dv = ref.backward_head(q, k, v, do, causal, scale)
+        return dq / scale, dk, dv
+
+    def wrong_d_sign(q, k, v, do, causal, scale):
+        s = ref.scores(q, k, scale, causal)
+        p, _, _ = ref.softmax_stats(s)
+        dp = do @ v.T
+        ds = p * (dp + np.sum(p * dp, axis=1)[:, None])
+        return scale * ds @ k, scale * ds.T @ q, p.T @ do
+
+    def transposed_dv(q, k, v, do, causal, scale):
+        dq, dk, _ = ref.backward_head(q, k, v, do, causal, scale)
+        s = ref.scores(q, k, scale, causal)
+        p, _, _ = ref.softmax_stats(s)
+        return dq, dk, p @ do
+
+    def dropped_d(q, k, v, do, causal, scale):
+        s = ref.scores(q, k, scale, causal)
+        p, _, _ = ref.softmax_stats(s)
+        ds = p * (do @ v.T)
+        return scale * ds @ k, scale * ds.T @ q, p.T @ do
+
+    for bad in (no_scale_on_dq, wrong_d_sign, transposed_dv, dropped_d):
+        assert not _fd_pin(bad), bad.__name__
+
+
+def test_pins_catch_planted_forward_mistakes(worked):
+    """A wrong rescale factor in the recurrence fails the worked-example pin."""
+    s = np.array(worked["scores"], dtype=np.float64)
+    v = np.array(worked["V"], dtype=np.float64)
+    page = worked["after_block"][-1]
+    num = sum(math.exp(a - b) * v[r] for a, b, r in page["o_numerator"])
+    o_page = num / _page_sum(page["o_denominator"])
+
+    def recurrence(alpha_sign):
+        m, l, o = -np.inf, 0.0, np.zeros(2)
+        for st in range(0, 4, 2):
+            blk = s[st:st + 2]
+            m_i = blk.max()
+            p_i = np.exp(blk - m_i)
+            m_new = max(m, m_i)
+            a_old = math.exp(alpha_sign * (m - m_new)) if m > -np.inf else 0.0
+            a_new = math.exp(m_i - m_new)
+            l_new = a_old * l + a_new * p_i.sum()
+            o = (l * a_old * o + a_new * (p_i @ v[st:st + 2])) / l_new
+            m, l = m_new, l_new
+        return o
+
+    np.testing.assert_allclose(recurrence(+1), o_page, rtol=1e-14)
+    assert not np.allclose(recurrence(-1), o_page, rtol=1e-6)

@@ -1,0 +1,107 @@
+"""Seeded synthetic inputs for the attention problems (no attention arithmetic).
+
+Shared by the oracle-side tests, the GPU parity tests and bench.py.  This
+module only draws and rounds random numbers; it computes nothing of the
+method.  Tensors are CPU torch tensors of shape [B, H, N, d] in the problem's
+dtype, drawn in fp32 from one ``torch.Generator`` per problem in the order
+Q, K, V, dO and rounded once to the dtype (round to nearest even).
+
+Problems (named by what they are):
+
+* ``single_head_f32``      B=1  H=1  N=256   d=64  fp32, non-causal, forward
+* ``gpt2_small_bf16``      B=8  H=12 N=1024  d=64  bf16, non-causal, forward
+* ``causal_4k_d128``       B=4  H=32 N=4096  d=128 bf16, causal, forward
+* ``causal_16k_d128``      B=1  H=32 N=16384 d=128 bf16, causal; Q, K, V
+  drawn N(0,1)*0.5, then in every (b, h) a random 1% of K rows (164 of
+  16384) multiplied by 8 to make later key blocks raise the running max
+* ``causal_bwd_4k_d64``    B=4  H=16 N=4096  d=64  bf16, causal, backward
+  (dO ~ N(0,1))
+* ``causal_16k_d128_bwd``  the 16K problem above plus dO ~ N(0,1)
+* ``causal_4k_d128_bwd``   the 4K d=128 problem plus dO ~ N(0,1)
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Problem:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str          # "f32" or "bf16"
+    causal: bool
+    seed: int
+    backward: bool = False
+    qkv_mult: float = 1.0
+    stress_frac: float = 0.0
+    stress_mult: float = 1.0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def fwd_flops(self) -> float:
+        """4*B*H*N^2*d, halved when causal (the stated counting convention)."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def bwd_flops(self) -> float:
+        """2.5 x the forward count (the stated counting convention)."""
+        return 2.5 * self.fwd_flops()
+
+
+PROBLEMS: Dict[str, Problem] = {p.name: p for p in [
+    Problem("single_head_f32", 1, 1, 256, 64, "f32", False, 1001),
+    Problem("gpt2_small_bf16", 8, 12, 1024, 64, "bf16", False, 1002),
+    Problem("causal_4k_d128", 4, 32, 4096, 128, "bf16", True, 1003),
+    Problem("causal_16k_d128", 1, 32, 16384, 128, "bf16", True, 1004,
+            qkv_mult=0.5, stress_frac=0.01, stress_mult=8.0),
+    Problem("causal_bwd_4k_d64", 4, 16, 4096, 64, "bf16", True, 1005, backward=True),
+    Problem("causal_16k_d128_bwd", 1, 32, 16384, 128, "bf16", True, 1006,
+            backward=True, qkv_mult=0.5, stress_frac=0.01, stress_mult=8.0),
+    Problem("causal_4k_d128_bwd", 4, 32, 4096, 128, "bf16", True, 1007, backward=True),
+]}
+
+
+def make_inputs(p: Problem, *, with_do: Optional[bool] = None):
+    """Draw q, k, v (and do) for problem ``p``; returns a dict of CPU tensors."""
+    if with_do is None:
+        with_do = p.backward
+    g = torch.Generator(device="cpu")
+    g.manual_seed(p.seed)
+    shape = (p.B, p.H, p.N, p.d)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    if p.qkv_mult != 1.0:
+        q.mul_(p.qkv_mult)
+        k.mul_(p.qkv_mult)
+        v.mul_(p.qkv_mult)
+    if p.stress_frac > 0.0:
+        count = int(round(p.stress_frac * p.N))
+        for b in range(p.B):
+            for h in range(p.H):
+                rows = torch.randperm(p.N, generator=g)[:count]
+                k[b, h, rows] *= p.stress_mult
+    out = {"q": q, "k": k, "v": v}
+    if with_do:
+        out["do"] = torch.randn(shape, generator=g, dtype=torch.float32)
+    return {name: t.to(p.torch_dtype).contiguous() for name, t in out.items()}
+
+
+def random_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int,
+                  with_do: bool = False, mult: float = 1.0):
+    """Ad-hoc seeded N(0,1)*mult inputs for edge-case shapes (ragged N etc.)."""
+    p = Problem("adhoc", B, H, N, d, dtype, False, seed, backward=with_do, qkv_mult=mult)
+    return make_inputs(p)
