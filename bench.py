@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Throughput of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+fa_forward (O, lse) then the backward's three stages (D = rowsum(dO o O),
+the key-block accumulation of dK, dV and dQ, and the dQ conversion), on the
+long-context causal problem B=1, H=32, N=16384, d=128, bf16 (fp32
+accumulation).  Inputs are resident in HBM before timing starts.
+
+FLOP counting convention: forward 4*B*H*N^2*d, halved when causal; backward
+2.5x forward.  The value is total (forward + backward) FLOPs per step over
+the wall time of a step, in TFLOP/s.
+
+Prints ONE JSON line.  Options: --gpus N (only 1: the path runs on one GPU),
+--steps K, --warmup W, --no-cpu-baseline, --no-extra.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak at N=4K/16K, d=128"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0         # MI355X published HBM3E bandwidth
+KERNEL_SOURCES = ["fa_common.h", "fa_fwd.hip", "fa_bwd.hip"]
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "io_aware_tiled_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None.
+
+    profiles/hbm_traffic.json holds FETCH_SIZE / WRITE_SIZE per dispatch,
+    already scaled by the copy-kernel calibration, with the digest of the
+    kernel sources they were taken on; stale counters (sources changed since)
+    are not reported.
+    """
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("source_digest") != kernel_source_digest():
+        return None
+    ent = data.get("kernels", {}).get(kernel)
+    if not ent:
+        return None
+    return float(ent["fetch_bytes"]) + float(ent["write_bytes"])
+
+
+class Step:
+    """Pre-bound raw C-ABI calls of one step on torch's current stream."""
+
+    def __init__(self, fa, torch, inputs, p, dev):
+        self.torch = torch
+        self.p = p
+        self.q, self.k, self.v, self.do = (inputs[n].to(dev) for n in ("q", "k", "v", "do"))
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((p.B, p.H, p.N), dtype=torch.float32, device=dev)
+        self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
+        self.ws_bytes = fa.workspace_size(p.B, p.H, p.N, p.d)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.lib = fa.load_library()
+        self.stream = torch.cuda.current_stream(dev).cuda_stream
+        self.dt = fa.FA_BF16 if p.dtype == "bf16" else fa.FA_F32
+        self.dev = dev
+
+    def _ck(self, st, name):
+        if st != 0:
+            raise RuntimeError(f"{name} returned {st}: {self.lib.fa_strerror(st).decode()}")
+
+    def forward(self):
+        p = self
+        self._ck(self.lib.fa_forward(p.q.data_ptr(), p.k.data_ptr(), p.v.data_ptr(), p.o.data_ptr(),
+                                     p.lse.data_ptr(), self.p.B, self.p.H, self.p.N, self.p.d,
+                                     int(self.p.causal), self.p.scale, self.dt, self.stream), "fa_forward")
+
+    def bwd_pre(self):
+        self._ck(self.lib.fa_backward_preprocess(self.o.data_ptr(), self.do.data_ptr(), self.p.B, self.p.H,
+                                                 self.p.N, self.p.d, self.dt, self.ws.data_ptr(),
+                                                 self.ws_bytes, self.stream), "fa_backward_preprocess")
+
+    def bwd_main(self):
+        p = self
+        self._ck(self.lib.fa_backward_accumulate(p.q.data_ptr(), p.k.data_ptr(), p.v.data_ptr(),
+                                                 p.do.data_ptr(), p.lse.data_ptr(), p.dk.data_ptr(),
+                                                 p.dv.data_ptr(), self.p.B, self.p.H, self.p.N, self.p.d,
+                                                 int(self.p.causal), self.p.scale, self.dt, p.ws.data_ptr(),
+                                                 self.ws_bytes, self.stream), "fa_backward_accumulate")
+
+    def bwd_final(self):
+        self._ck(self.lib.fa_backward_finalize(self.dq.data_ptr(), self.p.B, self.p.H, self.p.N, self.p.d,
+                                               self.p.scale, self.dt, self.ws.data_ptr(), self.ws_bytes,
+                                               self.stream), "fa_backward_finalize")
+
+    STAGES = ("fwd", "bwd_pre", "bwd_main", "bwd_final")
+
+    def run(self, events=None):
+        fns = (self.forward, self.bwd_pre, self.bwd_main, self.bwd_final)
+        if events is None:
+            for fn in fns:
+                fn()
+            return
+        events[0].record()
+        for i, fn in enumerate(fns):
+            fn()
+            events[i + 1].record()
+
+
+def time_steps(step, torch, steps, warmup):
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step.run(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per = {name: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, name in enumerate(Step.STAGES)}
+    avg = {name: sum(v) / len(v) for name, v in per.items()}
+    return (t1 - t0) * 1e3 / steps, avg
+
+
+def kernel_table(p, avg):
+    fwd_f, bwd_f = p.fwd_flops(), p.bwd_flops()
+    elt = 2 if p.dtype == "bf16" else 4
+    rows = p.B * p.H * p.N
+    tens = rows * p.d * elt
+    out = {}
+    out["fwd"] = {"kernel": "fa_fwd_kernel", "ms": avg["fwd"], "flops": fwd_f,
+                  "tflops": fwd_f / avg["fwd"] * 1e-9, "frac_peak": fwd_f / avg["fwd"] * 1e-9 / PEAK_BF16_TFLOPS}
+    out["bwd_main"] = {"kernel": "fa_bwd_main_kernel", "ms": avg["bwd_main"], "flops": bwd_f,
+                       "tflops": bwd_f / avg["bwd_main"] * 1e-9,
+                       "frac_peak": bwd_f / avg["bwd_main"] * 1e-9 / PEAK_BF16_TFLOPS}
+    # memory-bound helpers: algorithmic bytes = each operand touched once
+    pre_bytes = 2 * tens + rows * 4 + rows * p.d * 4           # read O, dO; write D, zero dQ_acc
+    fin_bytes = rows * p.d * 4 + tens                          # read dQ_acc, write dQ
+    out["bwd_pre"] = {"kernel": "fa_bwd_pre_kernel", "ms": avg["bwd_pre"], "bytes": pre_bytes,
+                      "gbs": pre_bytes / avg["bwd_pre"] * 1e-6}
+    out["bwd_final"] = {"kernel": "fa_bwd_dq_kernel", "ms": avg["bwd_final"], "bytes": fin_bytes,
+                        "gbs": fin_bytes / avg["bwd_final"] * 1e-6}
+    out["bwd_total"] = {"ms": avg["bwd_pre"] + avg["bwd_main"] + avg["bwd_final"]}
+    out["bwd_total"]["tflops"] = bwd_f / out["bwd_total"]["ms"] * 1e-9
+    out["bwd_total"]["frac_peak"] = out["bwd_total"]["tflops"] / PEAK_BF16_TFLOPS
+    return out
+
+
+def cpu_baseline(inputs, p, heads):
+    """The fp64 oracle on a bounded sample: `heads` whole heads of the workload.
+
+    Each head's forward and backward (standard attention with materialised
+    S and P, naive chain rule) is timed as the oracle stands.
+    """
+    from oracle import attention_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001 - reporting only
+        threads = 1
+    import torch
+    heads = max(1, min(heads, p.B * p.H))
+    dt = 0.0
+    for i in range(heads):
+        b, h = divmod(i, p.H)
+        q, k, v, do = (inputs[n][b, h].to(torch.float64).numpy() for n in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        ref.forward_head(q, k, v, causal=p.causal, scale=p.scale)
+        ref.backward_head(q, k, v, do, causal=p.causal, scale=p.scale)
+        dt += time.perf_counter() - t0
+    flops = heads * 4.0 * p.N * p.N * p.d / (2 if p.causal else 1) * 3.5
+    return {"value": flops / dt * 1e-12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"{heads} of the {p.B * p.H} heads of {p.name} (N={p.N}, d={p.d}), forward + backward "
+                      f"in fp64 numpy ({threads} BLAS threads, elementwise steps single-threaded; host has "
+                      f"{os.cpu_count()} logical cpus); FLOPs counted with the same convention as the GPU"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="causal_16k_d128_bwd")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4, help="whole heads timed on the CPU oracle")
+    ap.add_argument("--no-extra", action="store_true", help="skip the N=4K, d=128 side measurement")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported. Heads are independent, so several GPUs would each run this same kernel on "
+              "their share of the heads.", file=sys.stderr)
+        return 2
+
+    import torch
+    import io_aware_tiled_attention_amd as fa
+    from workloads import PROBLEMS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda", 0)
+    p = PROBLEMS[args.workload]
+    inputs = make_inputs(p, with_do=True)
+    step = Step(fa, torch, inputs, p, dev)
+    ms_step, avg = time_steps(step, torch, args.steps, args.warmup)
+    kt = kernel_table(p, avg)
+
+    total_flops = p.fwd_flops() + p.bwd_flops()
+    value = total_flops / ms_step * 1e-9
+    dom = max(("fwd", "bwd_main"), key=lambda k: kt[k]["ms"])
+    traffic = measured_traffic(kt[dom]["kernel"])
+    roofline = {"bound": "mfma", "kernel": kt[dom]["kernel"], "achieved": kt[dom]["tflops"],
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": kt[dom]["tflops"] / PEAK_BF16_TFLOPS,
+                "traffic": traffic, "flops_per_launch": kt[dom]["flops"], "avg_launch_ms": kt[dom]["ms"]}
+
+    extra = {}
+    if not args.no_extra:
+        p4 = PROBLEMS["causal_4k_d128_bwd"]
+        del step
+        torch.cuda.empty_cache()
+        s4 = Step(fa, torch, make_inputs(p4, with_do=True), p4, dev)
+        ms4, avg4 = time_steps(s4, torch, max(5, args.steps // 2), 3)
+        k4 = kernel_table(p4, avg4)
+        extra[p4.name] = {"B": p4.B, "H": p4.H, "N": p4.N, "d": p4.d, "causal": True, "ms_per_step": ms4,
+                          "fwd_tflops": k4["fwd"]["tflops"], "fwd_frac_peak": k4["fwd"]["frac_peak"],
+                          "bwd_tflops": k4["bwd_total"]["tflops"], "bwd_frac_peak": k4["bwd_total"]["frac_peak"]}
+        del s4
+        torch.cuda.empty_cache()
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
+        "config": {"workload": f"{p.name}: causal attention forward + backward", "B": p.B, "H": p.H,
+                   "N": p.N, "d": p.d, "causal": p.causal, "flops_per_step": total_flops,
+                   "accumulation": "fp32"},
+        "fwd": {"tflops": kt["fwd"]["tflops"], "frac_peak": kt["fwd"]["frac_peak"], "ms": kt["fwd"]["ms"]},
+        "bwd": {"tflops": kt["bwd_total"]["tflops"], "frac_peak": kt["bwd_total"]["frac_peak"],
+                "ms": kt["bwd_total"]["ms"]},
+        "kernels": kt,
+        "roofline": roofline,
+        "extra": extra,
+        "kernel_source_digest": kernel_source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inputs, p, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

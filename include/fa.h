@@ -1,0 +1,135 @@
+/*
+ * fa.h -- C ABI of the exact tiled-attention library for AMD MI355X (gfx950).
+ *
+ * The library computes exact attention O = softmax(scale * Q K^T) V for every
+ * (batch, head) pair, block by block with an online softmax so that the
+ * N x N score and probability matrices never reach device memory, and the
+ * matching backward pass that recomputes them from the stored per-row
+ * log-sum-exp.  Definitions:
+ *   - attention, S and P: "Overview of Flash Attention series", section
+ *     Standard Attention Implementation / Forward Pass; the 1/sqrt(d) scale
+ *     as in the "Transformer 入门" (Transformer primer) definitions;
+ *   - online softmax and output rescaling: "FlashAttention in NeurIPS 2022"
+ *     (coreui blog) section 2.1, and "Как работает FlashAttention
+ *     математически" sections 3-4;
+ *   - stored statistics and recomputation: "Overview of Flash Attention
+ *     series", sections Tiling and Forward Pass of flashattention (the
+ *     normaliser L_i), and section 5 of the aivaro.ru answer;
+ *   - gradients: "Overview of Flash Attention series", section Backward Pass
+ *     of flashattention (dV = P^T dO, dP = dO V^T, D_i = do_i . o_i,
+ *     dS = P o (dP - D), dq_i = sum_j dS_ij k_j, dk_j = sum_i dS_ij q_i).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or copies to the host, and keeps no
+ *     state between calls (calls are reentrant).
+ *   - Tensors Q, K, V, O, dO, dQ, dK, dV are contiguous row-major
+ *     [B, H, N, d] (d fastest) in the element type `dtype`; lse is
+ *     contiguous [B, H, N] float32.  Pointers must be 16-byte aligned.
+ *   - `causal` != 0 keeps key index <= query index (masked scores are -inf).
+ *   - `scale` multiplies Q K^T before the softmax (1/sqrt(d) for standard
+ *     attention); it must be finite and >= 0.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously; results are valid once the caller synchronises the
+ *     stream.
+ *   - Outputs must not alias inputs.
+ *   - B, H or N equal to 0 describes an empty problem: the call validates the
+ *     pointers it can, enqueues nothing and returns FA_OK.
+ *   - Arguments are validated before any HIP call: an invalid call returns a
+ *     non-zero fa_status and enqueues nothing.  FA_ERR_HIP reports a launch
+ *     failure (hipGetLastError after the launch).  No C++ exception crosses
+ *     this interface.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V, O, dO, dQ, dK, dV.  Accumulation is always fp32. */
+enum fa_dtype {
+  FA_F32 = 0,  /* IEEE float32 */
+  FA_BF16 = 1  /* bfloat16; outputs rounded to nearest even */
+};
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* a required pointer is NULL (non-empty problem) */
+  FA_ERR_SHAPE = 2,     /* B, H or N negative, or B*H*N*d overflows */
+  FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 */
+  FA_ERR_DTYPE = 4,     /* dtype is not an fa_dtype */
+  FA_ERR_SCALE = 5,     /* scale is NaN, infinite or negative */
+  FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than fa_backward_workspace_size */
+  FA_ERR_HIP = 7,       /* the HIP runtime reported an error at launch */
+  FA_ERR_ALIGN = 8      /* a tensor pointer is not 16-byte aligned */
+};
+
+/*
+ * Forward pass.  Q, K, V are [B,H,N,d]; writes O [B,H,N,d] (same dtype) and
+ * lse [B,H,N] (float32, lse_i = ln sum_j exp(scale * q_i . k_j) over the
+ * unmasked keys j -- the log of the normaliser L_i of "Overview of Flash
+ * Attention series", kept for the backward's recomputation).  Each workgroup
+ * owns a tile of query rows, keeps its running row max m, row sum l and the
+ * un-normalised output in registers while streaming K/V tiles through LDS
+ * (the Q-outer "V2" loop order of the Transformer primer), and divides by l
+ * once at the end.
+ */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, int causal, float scale, int dtype,
+               void* stream);
+
+/*
+ * Bytes of device workspace that fa_backward needs: the fp32 row terms
+ * D = rowsum(dO o O) ([B,H,N]) and an fp32 dQ accumulator ([B,H,N,d]),
+ * each 256-byte aligned.  Linear in N: no N x N buffer is ever used.
+ * Returns 0 for invalid or empty shapes.
+ */
+size_t fa_backward_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Backward pass.  Inputs: Q, K, V, O, dO [B,H,N,d] and lse [B,H,N] from
+ * fa_forward on the same Q, K, V, causal and scale.  Writes dQ, dK, dV
+ * [B,H,N,d] (same dtype).  `workspace` is a caller-owned device buffer of at
+ * least fa_backward_workspace_size(B,H,N,d) bytes, 256-byte aligned; its
+ * contents on entry are ignored and on exit are unspecified.  P is
+ * recomputed as exp(scale * Q K^T - lse) ("Как работает FlashAttention
+ * математически" section 5); dQ is accumulated in fp32 in the workspace and
+ * converted at the end, so dQ may differ between runs in the last bits.
+ */
+int fa_backward(const void* q, const void* k, const void* v, const void* o,
+                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                int B, int H, int N, int d, int causal, float scale, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The three stages that fa_backward enqueues, in order, for callers that
+ * schedule or time them separately.  Same arguments, layout and workspace
+ * as fa_backward; calling the three in order on one stream is exactly
+ * fa_backward.
+ *   fa_backward_preprocess: D_i = do_i . o_i (fp32, the row term of the
+ *     softmax Jacobian, "Overview of Flash Attention series", Backward Pass)
+ *     into the workspace, and zero the workspace's fp32 dQ accumulator.
+ *   fa_backward_accumulate: recompute S and P from lse key block by key
+ *     block, write dK and dV, and add (dS K) into the dQ accumulator.
+ *   fa_backward_finalize: dQ = scale * accumulator, rounded to dtype.
+ */
+int fa_backward_preprocess(const void* o, const void* dout, int B, int H, int N, int d, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+int fa_backward_accumulate(const void* q, const void* k, const void* v, const void* dout,
+                           const float* lse, void* dk, void* dv, int B, int H, int N, int d,
+                           int causal, float scale, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream);
+int fa_backward_finalize(void* dq, int B, int H, int N, int d, float scale, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static English description of an fa_status value (never NULL). */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,141 @@
+"""Exact IO-aware tiled attention for AMD MI355X (gfx950), forward and backward.
+
+Thin torch-facing binding over the C ABI of ``libfa_gfx950.so`` (see
+include/fa.h).  torch provides device memory and the current stream; every
+step of the computation runs in the library's HIP kernels.  Tensors are
+contiguous [B, H, N, d] in float32 or bfloat16 on a ROCm device; lse is
+[B, H, N] float32.
+
+    o, lse = forward(q, k, v, causal=True)
+    dq, dk, dv = backward(q, k, v, o, do, lse, causal=True)
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+from . import _lib
+from ._lib import (FA_BF16, FA_F32, FaError, fa_backward, fa_backward_accumulate, fa_backward_finalize,
+                   fa_backward_preprocess, fa_backward_workspace_size, fa_forward, fa_strerror)
+
+__all__ = ["forward", "backward", "workspace_size", "FaError", "FA_F32", "FA_BF16",
+           "fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_preprocess",
+           "fa_backward_accumulate", "fa_backward_finalize", "fa_strerror", "load_library",
+           "backward_stages"]
+
+
+def load_library():
+    """Load the HIP library now (raises if it has not been built)."""
+    return _lib.load()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.float32 or torch.bfloat16")
+
+
+def _check(name, t, shape, dtype, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+
+
+def _stream_ptr(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def forward(q, k, v, causal: bool = False, scale: Optional[float] = None,
+            out=None, lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """O = softmax(scale * Q K^T) V and lse = ln rowsum exp(scale * Q K^T)."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if q.device.type != "cuda":
+        raise ValueError("tensors must live on a ROCm device")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(name, t, q.shape, q.dtype, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check("out", out, q.shape, q.dtype, q.device)
+    _check("lse", lse, (B, H, N), torch.float32, q.device)
+    st = fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, N, d, causal, scale, _dtype_code(q), _stream_ptr(q.device))
+    if st != 0:
+        raise FaError(st, "fa_forward")
+    return out, lse
+
+
+def workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return fa_backward_workspace_size(B, H, N, d)
+
+
+def backward(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
+             dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV of O = attention(Q, K, V) for the upstream gradient dO."""
+    import torch
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(name, t, q.shape, q.dtype, q.device)
+    _check("lse", lse, (B, H, N), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, q.shape, q.dtype, q.device)
+    need = fa_backward_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                     causal, scale, _dtype_code(q), workspace.data_ptr(), workspace.numel(),
+                     _stream_ptr(q.device))
+    if st != 0:
+        raise FaError(st, "fa_backward")
+    return dq, dk, dv
+
+
+def backward_stages(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
+                    dq=None, dk=None, dv=None, workspace=None):
+    """The same result as :func:`backward`, through the three staged entry points."""
+    import torch
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(name, t, q.shape, q.dtype, q.device)
+    _check("lse", lse, (B, H, N), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    need = fa_backward_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dt, s, ws, wn = _dtype_code(q), _stream_ptr(q.device), workspace.data_ptr(), workspace.numel()
+    st = fa_backward_preprocess(o.data_ptr(), do.data_ptr(), B, H, N, d, dt, ws, wn, s)
+    if st != 0:
+        raise FaError(st, "fa_backward_preprocess")
+    st = fa_backward_accumulate(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                                dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale, dt, ws, wn, s)
+    if st != 0:
+        raise FaError(st, "fa_backward_accumulate")
+    st = fa_backward_finalize(dq.data_ptr(), B, H, N, d, scale, dt, ws, wn, s)
+    if st != 0:
+        raise FaError(st, "fa_backward_finalize")
+    return dq, dk, dv

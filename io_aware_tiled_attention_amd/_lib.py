@@ -1,0 +1,98 @@
+"""ctypes loader for libfa_gfx950.so and the raw C-ABI entry points.
+
+Argument marshalling only: the signatures mirror include/fa.h one to one.
+Loading fails loudly when the library has not been built; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_NAME = "libfa_gfx950.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+# enum fa_dtype / enum fa_status (include/fa.h)
+FA_F32 = 0
+FA_BF16 = 1
+STATUS = {
+    0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_DTYPE",
+    5: "FA_ERR_SCALE", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ALIGN",
+}
+EXPORTED = ("fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_preprocess",
+            "fa_backward_accumulate", "fa_backward_finalize", "fa_strerror")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = STATUS.get(status, str(status))
+        msg = load().fa_strerror(status).decode()
+        super().__init__(f"{where} failed with {name}: {msg}")
+
+
+def load() -> ctypes.CDLL:
+    """Load (once) and return the HIP attention library."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first with "
+                "`python -m io_aware_tiled_attention_amd.build` (there is no fallback path)")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        lib.fa_forward.restype = i
+        lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+        lib.fa_backward.restype = i
+        lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
+        lib.fa_backward_workspace_size.restype = sz
+        lib.fa_backward_preprocess.argtypes = [vp, vp, i, i, i, i, i, vp, sz, vp]
+        lib.fa_backward_preprocess.restype = i
+        lib.fa_backward_accumulate.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+        lib.fa_backward_accumulate.restype = i
+        lib.fa_backward_finalize.argtypes = [vp, i, i, i, i, f, i, vp, sz, vp]
+        lib.fa_backward_finalize.restype = i
+        lib.fa_strerror.argtypes = [i]
+        lib.fa_strerror.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def fa_forward(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream) -> int:
+    return load().fa_forward(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), dtype, stream)
+
+
+def fa_backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype,
+                workspace, workspace_bytes, stream) -> int:
+    return load().fa_backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, int(causal),
+                              float(scale), dtype, workspace, workspace_bytes, stream)
+
+
+def fa_backward_preprocess(o, dout, B, H, N, d, dtype, workspace, workspace_bytes, stream) -> int:
+    return load().fa_backward_preprocess(o, dout, B, H, N, d, dtype, workspace, workspace_bytes, stream)
+
+
+def fa_backward_accumulate(q, k, v, dout, lse, dk, dv, B, H, N, d, causal, scale, dtype,
+                           workspace, workspace_bytes, stream) -> int:
+    return load().fa_backward_accumulate(q, k, v, dout, lse, dk, dv, B, H, N, d, int(causal),
+                                         float(scale), dtype, workspace, workspace_bytes, stream)
+
+
+def fa_backward_finalize(dq, B, H, N, d, scale, dtype, workspace, workspace_bytes, stream) -> int:
+    return load().fa_backward_finalize(dq, B, H, N, d, float(scale), dtype, workspace,
+                                       workspace_bytes, stream)
+
+
+def fa_backward_workspace_size(B, H, N, d) -> int:
+    return load().fa_backward_workspace_size(B, H, N, d)
+
+
+def fa_strerror(status: int) -> str:
+    return load().fa_strerror(status).decode()

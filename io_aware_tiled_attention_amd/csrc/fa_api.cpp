@@ -1,0 +1,136 @@
+// fa_api.cpp -- the C ABI declared in include/fa.h: validation, workspace
+// carve-up and dispatch to the HIP launchers.  Every argument is checked
+// before the first HIP call, so an invalid call enqueues nothing; no C++
+// exception crosses the interface.
+#include "fa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape check shared by every entry point; `empty` is set for B*H*N == 0.
+int check_shape(int B, int H, int N, int d, int dtype, float scale, bool* empty) {
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+  // B*H*N*d elements and B*H*N rows must fit the kernels' index arithmetic:
+  // rows and per-head offsets use 32-bit ints, whole-tensor offsets 64-bit.
+  const int64_t rows = (int64_t)B * H * N;
+  const int64_t tiles = ((int64_t)N + 127) / 128 * B * H;   // workgroups of the largest grid
+  if ((int64_t)B * H > INT32_MAX || (int64_t)N * d > INT32_MAX || tiles > INT32_MAX ||
+      rows > ((int64_t)1 << 40))
+    return FA_ERR_SHAPE;
+  *empty = rows == 0;
+  return FA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+// Validation and launch for any subset of the backward stages.  A pointer is
+// required (non-NULL, 16-byte aligned) exactly when a requested stage reads
+// or writes it.
+int run_backward(int stages, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal,
+                 float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  const int st = check_shape(B, H, N, d, dtype, scale, &empty);
+  if (st != FA_OK) return st;
+  if (empty) return FA_OK;
+  const bool pre = stages & fa::kStagePre, mid = stages & fa::kStageMain, fin = stages & fa::kStageFinal;
+  const void* need[9];
+  int n_need = 0;
+  if (pre) {
+    need[n_need++] = o;
+    need[n_need++] = dout;
+  }
+  if (mid) {
+    const void* ptrs[] = {q, k, v, lse, dk, dv};
+    for (const void* p : ptrs) need[n_need++] = p;
+    if (!pre) need[n_need++] = dout;
+  }
+  if (fin) need[n_need++] = dq;
+  for (int i = 0; i < n_need; ++i)
+    if (!need[i]) return FA_ERR_NULL;
+  for (int i = 0; i < n_need; ++i)
+    if (!aligned16(need[i])) return FA_ERR_ALIGN;
+  const size_t rows = (size_t)B * H * N;
+  const size_t bytes = fa::ws_dsum_bytes(rows) + fa::ws_dq_bytes(rows, (size_t)d);
+  if (!workspace || workspace_bytes < bytes) return FA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal ? 1 : 0, dtype, scale,
+                reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + fa::ws_dsum_bytes(rows))};
+  return hip_status(fa::launch_backward(a, stages, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+               int d, int causal, float scale, int dtype, void* stream) {
+  bool empty = false;
+  const int st = check_shape(B, H, N, d, dtype, scale, &empty);
+  if (st != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal ? 1 : 0, dtype, scale};
+  return hip_status(fa::launch_forward(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_backward_workspace_size(int B, int H, int N, int d) {
+  bool empty = false;
+  if (check_shape(B, H, N, d, FA_BF16, 1.f, &empty) != FA_OK || empty) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return fa::ws_dsum_bytes(rows) + fa::ws_dq_bytes(rows, (size_t)d);
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal,
+                float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_backward(fa::kStagePre | fa::kStageMain | fa::kStageFinal, q, k, v, o, dout, lse, dq, dk, dv, B,
+                      H, N, d, causal, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_backward_preprocess(const void* o, const void* dout, int B, int H, int N, int d, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return run_backward(fa::kStagePre, nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr, nullptr,
+                      B, H, N, d, 0, 1.f, dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_backward_accumulate(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                           void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return run_backward(fa::kStageMain, q, k, v, nullptr, dout, lse, nullptr, dk, dv, B, H, N, d, causal, scale,
+                      dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_backward_finalize(void* dq, int B, int H, int N, int d, float scale, int dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return run_backward(fa::kStageFinal, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dq, nullptr,
+                      nullptr, B, H, N, d, 0, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape: B, H or N negative, or the problem is too large";
+    case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
+    case FA_ERR_DTYPE: return "unsupported dtype: use FA_F32 or FA_BF16";
+    case FA_ERR_SCALE: return "invalid scale: must be finite and >= 0";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_backward_workspace_size()";
+    case FA_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned (workspace: 256-byte)";
+    default: return "unknown fa_status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+"""GPU parity of fa_forward against the fp64 oracle (needs an MI355X)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_tiled_attention_amd as fa
+from workloads import PROBLEMS, make_inputs, random_inputs
+
+from gpu_helpers import (TOL, TOL_LSE, announce, assert_close, check_forward_full, check_forward_rows,
+                         gpu_forward, require_gpu, to64)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example_softmax.json")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def test_single_head_f32_full():
+    p = PROBLEMS["single_head_f32"]
+    announce(p.name)
+    check_forward_full(make_inputs(p), p.causal, p.scale)
+
+
+def test_gpt2_small_bf16_full():
+    p = PROBLEMS["gpt2_small_bf16"]
+    announce(p.name)
+    check_forward_full(make_inputs(p), p.causal, p.scale)
+
+
+def test_causal_4k_d128_sampled():
+    p = PROBLEMS["causal_4k_d128"]
+    announce(p.name)
+    inputs = make_inputs(p)
+    o, lse = check_forward_rows(inputs, p.causal, p.scale, rows_per_head=24)
+    # and two whole heads
+    q, k, v = (to64(inputs[n]) for n in ("q", "k", "v"))
+    from oracle import attention_ref as ref
+    for b, h in [(0, 0), (3, 31)]:
+        o_ref, lse_ref = ref.forward_head(q[b, h], k[b, h], v[b, h], causal=True, scale=p.scale)
+        assert_close(f"O[{b},{h}]", o[b, h], o_ref, TOL["bf16"], bf16_output=True)
+        assert_close(f"lse[{b},{h}]", lse[b, h], lse_ref, TOL_LSE)
+
+
+def test_causal_16k_d128_stressed_sampled():
+    p = PROBLEMS["causal_16k_d128"]
+    announce(p.name)
+    inputs = make_inputs(p)
+    o, lse = check_forward_rows(inputs, p.causal, p.scale, rows_per_head=24)
+    q, k, v = (to64(inputs[n][0, 5]) for n in ("q", "k", "v"))
+    from oracle import attention_ref as ref
+    o_ref, lse_ref = ref.forward_head(q, k, v, causal=True, scale=p.scale)
+    assert_close("O[0,5]", o[0, 5], o_ref, TOL["bf16"], bf16_output=True)
+    assert_close("lse[0,5]", lse[0, 5], lse_ref, TOL_LSE)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 2, 63, 65, 129, 257])
+def test_ragged_lengths(n, causal, d, dtype):
+    announce(f"ragged N={n} d={d} causal={causal} {dtype}")
+    inputs = random_inputs(2, 3, n, d, dtype, seed=7000 + n + d)
+    check_forward_full(inputs, causal, 1.0 / math.sqrt(d))
+
+
+@pytest.mark.parametrize("n", [1000, 2049])
+def test_many_tiles_ragged_tail_bf16(n):
+    announce(f"many tiles N={n}")
+    inputs = random_inputs(1, 4, n, 128, "bf16", seed=n)
+    check_forward_full(inputs, True, 1.0 / math.sqrt(128))
+    check_forward_full(inputs, False, 1.0 / math.sqrt(128))
+
+
+def test_worked_example_on_gpu():
+    """The coreui worked example, embedded in an N=4, d=64 fp32 problem."""
+    announce("worked example")
+    page = json.load(open(GOLDEN))
+    s = np.array(page["scores"], dtype=np.float64)
+    vv = np.array(page["V"], dtype=np.float64)
+    den = math.fsum(math.exp(a - b) for a, b in page["softmax_shifted_denominator"])
+    o_page = sum(math.exp(a - b) * vv[r] for (a, b), r in zip(page["softmax_shifted_numerators"], range(4))) / den
+    lse_page = max(s) + math.log(den)
+    q = torch.zeros(1, 1, 4, 64)
+    q[..., 0] = 1.0
+    k = torch.zeros(1, 1, 4, 64)
+    k[0, 0, :, 0] = torch.tensor(page["scores"], dtype=torch.float32)
+    v = torch.zeros(1, 1, 4, 64)
+    v[0, 0, :, :2] = torch.tensor(page["V"], dtype=torch.float32)
+    o, lse = gpu_forward({"q": q, "k": k, "v": v}, False, 1.0)
+    for r in range(4):
+        assert_close(f"O row {r}", o[0, 0, r, :2], o_page, 1e-5)
+        assert_close(f"O row {r} rest", o[0, 0, r, 2:], np.zeros(62), 1e-5)
+        assert abs(float(lse[0, 0, r]) - lse_page) <= TOL_LSE
+
+
+def test_scale_zero_is_uniform_average():
+    announce("scale=0")
+    inputs = random_inputs(1, 2, 100, 64, "f32", seed=11)
+    for causal in (False, True):
+        o, lse = gpu_forward(inputs, causal, 0.0)
+        v = to64(inputs["v"])
+        n = v.shape[2]
+        cnt = np.arange(1, n + 1) if causal else np.full(n, n)
+        want = np.cumsum(v, axis=2) / cnt[:, None] if causal else np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+        assert_close("O", o, want, 1e-5)
+        assert_close("lse", lse, np.broadcast_to(np.log(cnt), lse.shape), 1e-5)
+
+
+def test_empty_problem_and_determinism():
+    announce("empty + determinism")
+    dev = torch.device("cuda", 0)
+    q = torch.zeros(1, 2, 0, 64, device=dev, dtype=torch.bfloat16)
+    o, lse = fa.forward(q, q, q)
+    assert o.shape == (1, 2, 0, 64) and lse.shape == (1, 2, 0)
+    inputs = random_inputs(2, 2, 300, 128, "bf16", seed=5)
+    o1, l1 = gpu_forward(inputs, True, 0.1)
+    o2, l2 = gpu_forward(inputs, True, 0.1)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_stream_argument_is_honoured():
+    announce("side stream")
+    inputs = random_inputs(1, 2, 512, 64, "bf16", seed=9)
+    dev = torch.device("cuda", 0)
+    q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
+    ref_o, ref_l = fa.forward(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(s):
+        o, l = fa.forward(q, k, v, causal=True)
+    s.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
