@@ -200,6 +200,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=4, help="whole heads timed on the CPU oracle")
     ap.add_argument("--no-extra", action="store_true", help="skip the N=4K, d=128 side measurement")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (reference for HBM counters)")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -217,6 +219,17 @@ def main(argv=None):
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         return 1
     dev = torch.device("cuda", 0)
+    if args.copy_calibration:
+        n = 1 << 28                       # 2**28 fp32 = 1 GiB per tensor
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read_per_copy": 4 * n, "bytes_written_per_copy": 4 * n,
+                                               "copies": 3}}), flush=True)
+        return 0
     p = PROBLEMS[args.workload]
     inputs = make_inputs(p, with_do=True)
     step = Step(fa, torch, inputs, p, dev)

@@ -18,14 +18,18 @@
 //   2. fa_bwd_main: a workgroup owns 128 keys (4 waves x 32) and keeps its
 //      slice of K, V and the fp32 accumulators dK^T, dV^T in registers while
 //      sweeping the query blocks that can see them (all blocks, or the blocks
-//      at or below the diagonal when causal).  Per query block each wave
-//      recomputes S and P for its 32 keys, forms dP and dS, and accumulates
-//      dV^T += dO^T P and dK^T += Q^T dS on the matrix cores (the P and dS
-//      registers are already in B-operand layout; Q^T and dO^T fragments come
-//      from the row-major LDS tiles through the gfx950 transpose read).  dS is
-//      then exchanged through LDS so that each wave forms one 32x32 tile of
-//      dQ = dS K over all 128 keys and adds it to the fp32 accumulator with
-//      atomics, one contribution per (query block, workgroup).
+//      at or below the diagonal when causal), BQ query rows at a time.  Per
+//      32-row sub-block each wave recomputes S and P for its 32 keys, forms dP
+//      and dS, and accumulates dV^T += dO^T P and dK^T += Q^T dS on the matrix
+//      cores (P and dS are already in B-operand layout; dO^T and Q^T come from
+//      the row-major LDS tiles through the gfx950 transpose read).  dS^T goes
+//      to LDS; in the next iteration each wave reads it back, transposed, as
+//      the A operand of dQ = dS K over all 128 keys and adds its tiles to the
+//      fp32 accumulator with buffer atomics -- one contribution per (query
+//      block, workgroup), one barrier per query block.
+//      Query blocks are swept from the last one downwards: all key tiles of a
+//      head run at the same time on one XCD and reach the same query block
+//      together, so their dQ atomics meet in that XCD's L2.
 //   3. fa_bwd_dq: dQ = scale * accumulator, rounded to the element type.
 // The loop order over (key block outer, query block inner) is the one whose
 // dK/dV stay on chip; the pages leave the backward loop order open.
@@ -41,42 +45,27 @@ constexpr int kBwdKW = 32;                      // keys per wave
 constexpr int kBwdBK = kBwdWaves * kBwdKW;      // keys per workgroup
 
 template <typename T, int D>
-struct BwdSmem {
+struct BwdCfg {
   static constexpr int ESZ = sizeof(T);
-  static constexpr int BQ = 32 * kBwdWaves * 32 / D;   // query rows per block: dQ tiles = waves
-  static constexpr int QB = BQ / 32;                   // 32-row query sub-blocks
-  static constexpr int QLD = D + 16 / ESZ;             // Q / dO row stride (elements)
-  static constexpr int SLD = kBwdBK + 16 / ESZ;        // dS row stride (elements)
-  // stage: Q tile, dO tile (T) then lse (in the exponent domain) and D (float)
-  static constexpr int QTILE_B = BQ * QLD * ESZ;
-  static constexpr int STAGE_B = 2 * QTILE_B + 2 * BQ * 4;
-  static constexpr int DS_B = BQ * SLD * ESZ;
-  static constexpr int BYTES = 2 * STAGE_B + DS_B;
-  static constexpr int VE = 16 / ESZ;
-  static constexpr int CPR = D / VE;
-  static constexpr int NCH = BQ * CPR / kBwdThreads;
-  static_assert(BQ * CPR % kBwdThreads == 0, "Q tile must split evenly over threads");
-  static_assert((D / 32) * QB == kBwdWaves, "one dQ tile per wave");
-  static_assert(QTILE_B % 16 == 0 && STAGE_B % 16 == 0, "16-byte aligned LDS regions");
+  static constexpr int BQ = ESZ == 2 ? 64 : 32;        // query rows per block
+  static constexpr int QB = BQ / 32;                   // 32-row sub-blocks
+  static constexpr int NDB = D / 32;                   // 32-wide d blocks
+  static constexpr int NDQ = NDB * QB;                 // 32x32 dQ tiles per block
+  static constexpr int TPW = (NDQ + kBwdWaves - 1) / kBwdWaves;   // dQ tiles per wave
+  static constexpr int QTILE = BQ * D * ESZ;           // bytes of the Q (or dO) tile
+  static constexpr int STATS = 2 * 64 * 4;             // lse, D: 64 floats each
+  static constexpr int STAGE = 2 * QTILE + STATS;
+  static constexpr int DST = kBwdBK * BQ * ESZ;        // dS^T tile [keys][queries]
+  static constexpr int BYTES = 2 * STAGE + 2 * DST;
+  static_assert(ESZ != 2 || kBwdBK * D * ESZ <= 2 * DST, "K staging fits in the dS^T buffers");
+  static_assert(NDB % 1 == 0 && (NDQ <= kBwdWaves || NDQ % kBwdWaves == 0), "dQ tiles split over waves");
+  static_assert(kBwdWaves % NDB == 0 || NDB % kBwdWaves == 0, "one d block per wave");
+  __device__ static lds_u8* q(lds_u8* b, int st) { return b + st * STAGE; }
+  __device__ static lds_u8* dout(lds_u8* b, int st) { return b + st * STAGE + QTILE; }
+  __device__ static lds_u8* lse(lds_u8* b, int st) { return b + st * STAGE + 2 * QTILE; }
+  __device__ static lds_u8* dd(lds_u8* b, int st) { return b + st * STAGE + 2 * QTILE + 256; }
+  __device__ static lds_u8* dst(lds_u8* b, int k) { return b + 2 * STAGE + k * DST; }
 };
-
-// Transposed A fragment (M = d, K = rows) from a row-major bf16 LDS tile:
-// lane l gets column dcol0 + l%32 of rows row0 + 8a + 4g + b (a in {0,1},
-// b in 0..3), matching the accumulator rows acc_row(8t + e, g) of a 32-row
-// sub-block when row0 = 16t.
-__device__ __forceinline__ bf16x8 load_tr_frag(const bf16* base, int ld, int row0, int dcol0, int lane) {
-  const int j = lane & 15;
-  const int h = (lane >> 4) & 1;
-  const int g = lane >> 5;
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const bf16* p0 = base + (row0 + 4 * g + (j >> 2)) * ld + dcol0 + 16 * h + 4 * (j & 3);
-  const bf16* p1 = p0 + 8 * ld;
-  union { s16x4 s[2]; bf16x8 b; } u;
-  u.s[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-  u.s[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
-  return u.b;
-}
 
 // ---------------------------------------------------------------- 1. preprocess
 template <typename T, int D>
@@ -91,11 +80,11 @@ void fa_bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, float*
   const int col = (tid % CPR) * VE;
   float part = 0.f;
   if (row < rows) {
-    Vec16<T> o, d;
-    o.raw = *reinterpret_cast<const uint4*>(O + row * D + col);
-    d.raw = *reinterpret_cast<const uint4*>(dO + row * D + col);
+    union { uint4 u; T t[VE]; } o, d;
+    o.u = *reinterpret_cast<const uint4*>(O + row * D + col);
+    d.u = *reinterpret_cast<const uint4*>(dO + row * D + col);
 #pragma unroll
-    for (int e = 0; e < VE; ++e) part += (float)o.get(e) * (float)d.get(e);
+    for (int e = 0; e < VE; ++e) part += (float)o.t[e] * (float)d.t[e];
     float4* z = reinterpret_cast<float4*>(dq_acc + row * D + col);
 #pragma unroll
     for (int e = 0; e < VE / 4; ++e) z[e] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -111,15 +100,20 @@ __global__ __launch_bounds__(kBwdThreads, 1)
 void fa_bwd_main_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                         const T* __restrict__ dO, const float* __restrict__ LSE,
                         const float* __restrict__ dsum, float* __restrict__ dq_acc,
-                        T* __restrict__ dK, T* __restrict__ dV, int N, int BH, float scale,
-                        float scale_log2) {
+                        T* __restrict__ dK, T* __restrict__ dV, int N, int BH, float scale) {
   using M = Mfma<T>;
-  using L = BwdSmem<T, D>;
+  using C = BwdCfg<T, D>;
+  using G = Tile<T, D>;                 // Q, dO and K tiles: rows x D
+  using GS = Tile<T, C::BQ>;            // dS^T tile: 128 key rows x BQ query columns
+  using X = ExpDomain<T>;
+  using Frag = typename M::Frag;
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
   constexpr int KPL = M::KPL, KC = M::KC;
-  constexpr int NDB = D / 32;
-  constexpr int BQ = L::BQ, QB = L::QB;
-  const float kfac = ExpDomain<T>::factor(scale, scale_log2);
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  constexpr int NDB = C::NDB, BQ = C::BQ, QB = C::QB;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
+  lds_u8* smem = (lds_u8*)smem_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -133,41 +127,43 @@ void fa_bwd_main_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
   const int kw0 = k0 + w * kBwdKW;
   const int mykey = kw0 + r32;
   const size_t head = (size_t)bh * N * D;
-  const T* Qh = Q + head;
-  const T* Kh = K + head;
-  const T* Vh = V + head;
-  const T* dOh = dO + head;
-  const float* lse_h = LSE + (size_t)bh * N;
-  const float* dsum_h = dsum + (size_t)bh * N;
-  float* dq_h = dq_acc + head;
+  const uint32_t head_bytes = (uint32_t)N * G::R;
+  const rsrc_t rq = make_rsrc(Q + head, head_bytes);
+  const rsrc_t rk = make_rsrc(K + head, head_bytes);
+  const rsrc_t rv = make_rsrc(V + head, head_bytes);
+  const rsrc_t rdo = make_rsrc(dO + head, head_bytes);
+  const rsrc_t rlse = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
+  const rsrc_t rdd = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
+  const rsrc_t rdq = make_rsrc(dq_acc + head, (uint32_t)N * D * 4u);
+  const float kfac = X::factor(scale);
 
   // K and V rows of this wave as B operands (column = key, KPL d-values of group g).
-  typename M::Frag kf[D / KC], vf[D / KC];
+  Frag kf[D / KC], vf[D / KC];
 #pragma unroll
   for (int c = 0; c < D / KC; ++c) {
-    const bool ok = mykey < N;
-    kf[c] = ok ? M::load(Kh + (size_t)mykey * D + c * KC + g * KPL) : M::zero();
-    vf[c] = ok ? M::load(Vh + (size_t)mykey * D + c * KC + g * KPL) : M::zero();
+    const int off = mykey * G::R + (c * KC + g * KPL) * (int)sizeof(T);
+    kf[c] = M::load(rk, off);
+    vf[c] = M::load(rv, off);
   }
-  // K^T for this wave's dQ tile (column d = dblk*32 + l%32, KPL keys of group g
-  // per step, all 128 keys of the workgroup) as the B operand of dQ = dS K.
+
+  // K^T for this wave's dQ tiles (column d = dblk*32 + l%32) as the B operand of
+  // dQ = dS K; k-step kc covers keys kc*KC.., in the order of the dS fragments.
   const int dblk = w % NDB;
-  const int qblk = w / NDB;
-  typename M::Frag ktf[kBwdBK / KC];
+  Frag ktf[kBwdBK / KC];
+  if constexpr (sizeof(T) == 2) {
+    // stage the workgroup's 128 K rows in the (not yet used) dS^T buffers and
+    // read them back transposed: lane gets keys kc*16 + 8a + 4g + b
+    lds_u8* kst = C::dst(smem, 0);
+    tile_to_lds<T, D, kBwdBK, kBwdWaves>(rk, kst, k0, w, lane);
+    wait_vmem();
+    __syncthreads();
 #pragma unroll
-  for (int kc = 0; kc < kBwdBK / KC; ++kc) {
-    if constexpr (sizeof(T) == 2) {
-      bf16x8 f;
+    for (int kc = 0; kc < kBwdBK / KC; ++kc) ktf[kc] = lds_tr_frag<D>(kst, kc * 16, dblk * 32, lane);
+    __syncthreads();
+  } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = k0 + kc * 16 + 8 * g + e;
-        f[e] = key < N ? Kh[(size_t)key * D + dblk * 32 + r32] : (bf16)0.f;
-      }
-      ktf[kc] = f;
-    } else {
-      const int key = k0 + kc * 2 + g;
-      ktf[kc] = key < N ? Kh[(size_t)key * D + dblk * 32 + r32] : 0.f;
-    }
+    for (int kc = 0; kc < kBwdBK / KC; ++kc)
+      ktf[kc] = M::load(rk, (k0 + kc * 2 + g) * G::R + (dblk * 32 + r32) * (int)sizeof(T));
   }
 
   f32x16 dv_acc[NDB], dk_acc[NDB];
@@ -177,180 +173,150 @@ void fa_bwd_main_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
     dk_acc[db] = f32x16{};
   }
 
-  T* ds_s = reinterpret_cast<T*>(smem_raw + 2 * L::STAGE_B);
-  auto stage_q = [&](int st) { return reinterpret_cast<T*>(smem_raw + st * L::STAGE_B); };
-  auto stage_do = [&](int st) { return reinterpret_cast<T*>(smem_raw + st * L::STAGE_B + L::QTILE_B); };
-  auto stage_lse = [&](int st) { return reinterpret_cast<float*>(smem_raw + st * L::STAGE_B + 2 * L::QTILE_B); };
-  auto stage_dd = [&](int st) { return stage_lse(st) + BQ; };
+  auto load_block = [&](int q0b, int st) {
+    tile_to_lds<T, D, BQ, kBwdWaves>(rq, C::q(smem, st), q0b, w, lane);
+    tile_to_lds<T, D, BQ, kBwdWaves>(rdo, C::dout(smem, st), q0b, w, lane);
+    // lse and D of the block's rows, one float per lane (rows past N read 0)
+    if (w == 0) lds_dma4(rlse, C::lse(smem, st), (q0b + lane) * 4);
+    if (w == 1) lds_dma4(rdd, C::dd(smem, st), (q0b + lane) * 4);
+  };
 
-  uint4 qreg[L::NCH], doreg[L::NCH];
-  float lse_reg = 0.f, dd_reg = 0.f;
-  auto load_block = [&](int q0b) {
+  // dQ tiles of the block whose dS^T is in buffer `buf`: tile t = w + 4u covers
+  // d block t % NDB (= dblk) and query sub-block t / NDB.
+  auto dq_block = [&](int q0b, int buf) {
+    const lds_u8* ds = C::dst(smem, buf);
 #pragma unroll
-    for (int r = 0; r < L::NCH; ++r) {
-      const int c = tid + r * kBwdThreads;
-      const int row = c / L::CPR;
-      const int col = (c % L::CPR) * L::VE;
-      const int q = q0b + row;
-      if (q < N) {
-        qreg[r] = *reinterpret_cast<const uint4*>(Qh + (size_t)q * D + col);
-        doreg[r] = *reinterpret_cast<const uint4*>(dOh + (size_t)q * D + col);
-      } else {
-        qreg[r] = make_uint4(0, 0, 0, 0);
-        doreg[r] = make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < C::TPW; ++u) {
+      const int t = w + kBwdWaves * u;
+      if (t < C::NDQ) {
+        const int qblk = t / NDB;
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < kBwdBK / KC; ++kc) {
+          Frag a;
+          if constexpr (sizeof(T) == 2) a = lds_tr_frag<BQ>(ds, kc * 16, qblk * 32, lane);
+          else a = M::lds(ds + GS::off(kc * 2 + g, qblk * 32 + r32));
+          acc = M::mma(a, ktf[kc], acc);
+        }
+        // lane holds column d = dblk*32 + r32 of query rows acc_row(i, g)
+        const int qrow = q0b + qblk * 32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          atomic_add_f32(rdq, ((qrow + acc_row(i, g)) * D + dblk * 32 + r32) * 4, acc[i]);
       }
     }
-    if (tid < BQ) {
-      const int q = q0b + tid;
-      // rows past the end get lse = +inf, hence P = 0
-      lse_reg = q < N ? ExpDomain<T>::from_lse(lse_h[q]) : __builtin_inff();
-      dd_reg = q < N ? dsum_h[q] : 0.f;
-    }
-  };
-  auto store_block = [&](int st) {
-    T* qs = stage_q(st);
-    T* dos = stage_do(st);
-#pragma unroll
-    for (int r = 0; r < L::NCH; ++r) {
-      const int c = tid + r * kBwdThreads;
-      const int row = c / L::CPR;
-      const int col = (c % L::CPR) * L::VE;
-      *reinterpret_cast<uint4*>(qs + row * L::QLD + col) = qreg[r];
-      *reinterpret_cast<uint4*>(dos + row * L::QLD + col) = doreg[r];
-    }
-    if (tid < BQ) {
-      stage_lse(st)[tid] = lse_reg;
-      stage_dd(st)[tid] = dd_reg;
-    }
   };
 
-  const int q_begin = CAUSAL ? k0 : 0;   // queries below k0 see none of these keys
-  const int nblocks = (N - q_begin + BQ - 1) / BQ;
+  // Query blocks from the last one down to the first that sees these keys.
+  const int nqb_total = (N + BQ - 1) / BQ;
+  const int qb_first = CAUSAL ? k0 / BQ : 0;
+  const int nblocks = nqb_total - qb_first;
+  auto block_start = [&](int it) { return (nqb_total - 1 - it) * BQ; };
 
-  load_block(q_begin);
-  store_block(0);
+  load_block(block_start(0), 0);
+  wait_vmem();
   __syncthreads();
 
-  for (int jb = 0; jb < nblocks; ++jb) {
-    const int q0b = q_begin + jb * BQ;
-    const int st = jb & 1;
-    if (jb + 1 < nblocks) load_block(q0b + BQ);
+  for (int it = 0; it < nblocks; ++it) {
+    const int q0b = block_start(it);
+    const int st = it & 1;
+    if (it + 1 < nblocks) load_block(block_start(it + 1), st ^ 1);
+    if (it > 0) dq_block(block_start(it - 1), st ^ 1);
 
-    const T* qs = stage_q(st);
-    const T* dos = stage_do(st);
-    const float* lse_s = stage_lse(st);
-    const float* dd_s = stage_dd(st);
+    const lds_u8* qs = C::q(smem, st);
+    const lds_u8* dos = C::dout(smem, st);
+    const lds_u8* lse_s = C::lse(smem, st);
+    const lds_u8* dd_s = C::dd(smem, st);
+    lds_u8* ds_out = C::dst(smem, st);
 
-    const bool skip = CAUSAL && (q0b + BQ - 1 < kw0);   // every query precedes every key of the wave
-    if (!skip) {
-      const bool masked = (CAUSAL && q0b < kw0 + kBwdKW - 1) || (kw0 + kBwdKW > N);
 #pragma unroll
-      for (int qs_i = 0; qs_i < QB; ++qs_i) {
-        // S = Q K^T and dP = dO V^T: rows = queries, column = this lane's key.
-        f32x16 s = f32x16{}, dp = f32x16{};
+    for (int qs_i = 0; qs_i < QB; ++qs_i) {
+      const int qsb = q0b + qs_i * 32;
+      if (CAUSAL && qsb + 31 < kw0) {
+        // every query of the sub-block precedes every key of the wave: dS = 0
 #pragma unroll
-        for (int c = 0; c < D / KC; ++c) {
-          typename M::Frag aq = M::load(qs + (qs_i * 32 + r32) * L::QLD + c * KC + g * KPL);
-          typename M::Frag ado = M::load(dos + (qs_i * 32 + r32) * L::QLD + c * KC + g * KPL);
-          s = M::mma(aq, kf[c], s);
-          dp = M::mma(ado, vf[c], dp);
+        for (int a = 0; a < 4; ++a) {
+          const int off = GS::off(w * kBwdKW + r32, qs_i * 32 + 8 * a + 4 * g);
+          if constexpr (sizeof(T) == 2) *(lds_u32x2*)(ds_out + off) = u32x2{0u, 0u};
+          else *(lds_u32x4*)(ds_out + off) = u32x4{0u, 0u, 0u, 0u};
         }
-        // P = exp(S - lse) and dS = P (dP - D), row by row of the accumulator.
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ql = qs_i * 32 + acc_row(i, g);
-          float p = ExpDomain<T>::ex(__builtin_fmaf(s[i], kfac, -lse_s[ql]));
-          if (masked) {
-            const int q = q0b + ql;
-            const bool out = (mykey >= N) || (CAUSAL && mykey > q);
-            p = out ? 0.f : p;
-          }
-          s[i] = p;
-          dp[i] = p * (dp[i] - dd_s[ql]);
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS (k = the 32 queries of the sub-block).
-#pragma unroll
-        for (int t = 0; t < 32 / KC; ++t) {
-          typename M::Frag pb = M::pack(s, t);
-          typename M::Frag dsb = M::pack(dp, t);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            typename M::Frag a_do, a_q;
-            if constexpr (sizeof(T) == 2) {
-              a_do = load_tr_frag(reinterpret_cast<const bf16*>(dos), L::QLD, qs_i * 32 + 16 * t, db * 32, lane);
-              a_q = load_tr_frag(reinterpret_cast<const bf16*>(qs), L::QLD, qs_i * 32 + 16 * t, db * 32, lane);
-            } else {
-              const int row = qs_i * 32 + acc_row(t, g);
-              a_do = dos[row * L::QLD + db * 32 + r32];
-              a_q = qs[row * L::QLD + db * 32 + r32];
-            }
-            dv_acc[db] = M::mma(a_do, pb, dv_acc[db]);
-            dk_acc[db] = M::mma(a_q, dsb, dk_acc[db]);
-          }
-        }
-        // dS to LDS as [query][key] for the dQ product.
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          ds_s[(qs_i * 32 + acc_row(i, g)) * L::SLD + w * kBwdKW + r32] = (T)dp[i];
+        continue;
       }
-    } else {
+      // S = Q K^T and dP = dO V^T: rows = queries, column = this lane's key.
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int qs_i = 0; qs_i < QB; ++qs_i)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          ds_s[(qs_i * 32 + acc_row(i, g)) * L::SLD + w * kBwdKW + r32] = (T)0.f;
-    }
-    __syncthreads();
-
-    // dQ tile (queries qblk*32.., d dblk*32..) = dS K over the 128 keys.
-    {
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int kc = 0; kc < kBwdBK / KC; ++kc) {
-        typename M::Frag a = M::load(ds_s + (qblk * 32 + r32) * L::SLD + kc * KC + g * KPL);
-        acc = M::mma(a, ktf[kc], acc);
+      for (int c = 0; c < D / KC; ++c) {
+        const int off = G::off(qs_i * 32 + r32, c * KC + g * KPL);
+        s = M::mma(M::lds(qs + off), kf[c], s);
+        dp = M::mma(M::lds(dos + off), vf[c], dp);
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = q0b + qblk * 32 + acc_row(i, g);
-        if (q < N) unsafeAtomicAdd(dq_h + (size_t)q * D + dblk * 32 + r32, acc[i]);
-      }
-    }
-
-    if (jb + 1 < nblocks) store_block(st ^ 1);
-    __syncthreads();
-  }
-
-  // dK = scale * dK_acc, dV = dV_acc; lane holds key mykey, d = db*32 + acc_row(i, g).
-  if (mykey < N) {
-    T* dk_row = dK + head + (size_t)mykey * D;
-    T* dv_row = dV + head + (size_t)mykey * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      // P = exp(S - lse), dS = P (dP - D); masked entries (key > query, or a
+      // key past the end) get P = 0.
+      const bool masked = (CAUSAL && qsb < kw0 + kBwdKW - 1) || (kw0 + kBwdKW > N);
+      const int lim = (mykey >= N) ? 64 : (CAUSAL ? mykey - (qsb + 4 * g) : -1);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int d0 = db * 32 + 8 * a + 4 * g;
-        if constexpr (sizeof(T) == 2) {
-          bf16x4 k4, v4;
+        const f32x4 lz = *(const lds_f32x4*)(lse_s + (qs_i * 32 + 8 * a + 4 * g) * 4);
+        const f32x4 dz = *(const lds_f32x4*)(dd_s + (qs_i * 32 + 8 * a + 4 * g) * 4);
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            k4[b] = (bf16)(dk_acc[db][4 * a + b] * scale);
-            v4[b] = (bf16)dv_acc[db][4 * a + b];
-          }
-          *reinterpret_cast<bf16x4*>(dk_row + d0) = k4;
-          *reinterpret_cast<bf16x4*>(dv_row + d0) = v4;
-        } else {
-          f32x4 k4, v4;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            k4[b] = dk_acc[db][4 * a + b] * scale;
-            v4[b] = dv_acc[db][4 * a + b];
-          }
-          *reinterpret_cast<f32x4*>(dk_row + d0) = k4;
-          *reinterpret_cast<f32x4*>(dv_row + d0) = v4;
+        for (int b = 0; b < 4; ++b) {
+          const int i = 4 * a + b;
+          float p = X::ex(__builtin_fmaf(s[i], kfac, -X::from_lse(lz[b])));
+          if (masked) p = (acc_row(i, 0) < lim) ? 0.f : p;
+          s[i] = p;
+          dp[i] = p * (dp[i] - dz[b]);
         }
       }
+      // dV^T += dO^T P and dK^T += Q^T dS (k = the 32 queries of the sub-block).
+#pragma unroll
+      for (int t = 0; t < 32 / KC; ++t) {
+        const Frag pb = M::pack(s, t);
+        const Frag dsb = M::pack(dp, t);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          Frag a_do, a_q;
+          if constexpr (sizeof(T) == 2) {
+            a_do = lds_tr_frag<D>(dos, qs_i * 32 + 16 * t, db * 32, lane);
+            a_q = lds_tr_frag<D>(qs, qs_i * 32 + 16 * t, db * 32, lane);
+          } else {
+            const int off = G::off(qs_i * 32 + acc_row(t, g), db * 32 + r32);
+            a_do = M::lds(dos + off);
+            a_q = M::lds(qs + off);
+          }
+          dv_acc[db] = M::mma(a_do, pb, dv_acc[db]);
+          dk_acc[db] = M::mma(a_q, dsb, dk_acc[db]);
+        }
+      }
+      // dS^T (row = key, 4 consecutive query columns per store) for the dQ product.
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int off = GS::off(w * kBwdKW + r32, qs_i * 32 + 8 * a + 4 * g);
+        if constexpr (sizeof(T) == 2) {
+          const bf16x4 v4 = {(bf16)dp[4 * a], (bf16)dp[4 * a + 1], (bf16)dp[4 * a + 2], (bf16)dp[4 * a + 3]};
+          *(lds_u32x2*)(ds_out + off) = __builtin_bit_cast(u32x2, v4);
+        } else {
+          const f32x4 v4 = {dp[4 * a], dp[4 * a + 1], dp[4 * a + 2], dp[4 * a + 3]};
+          *(lds_u32x4*)(ds_out + off) = __builtin_bit_cast(u32x4, v4);
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
   }
+  dq_block(block_start(nblocks - 1), (nblocks - 1) & 1);
+
+  // dK = scale * dK_acc, dV = dV_acc; lane holds key mykey, d = db*32 + acc_row(i, g).
+  const rsrc_t rdk = make_rsrc(dK + head, head_bytes);
+  const rsrc_t rdv = make_rsrc(dV + head, head_bytes);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int off = mykey * G::R + (db * 32 + 8 * a + 4 * g) * (int)sizeof(T);
+      store4<T>(rdk, off, dk_acc[db][4 * a] * scale, dk_acc[db][4 * a + 1] * scale, dk_acc[db][4 * a + 2] * scale,
+                dk_acc[db][4 * a + 3] * scale);
+      store4<T>(rdv, off, dv_acc[db][4 * a], dv_acc[db][4 * a + 1], dv_acc[db][4 * a + 2], dv_acc[db][4 * a + 3]);
+    }
 }
 
 // ---------------------------------------------------------------- 3. dQ finalise
@@ -361,11 +327,7 @@ void fa_bwd_dq_kernel(const float* __restrict__ dq_acc, T* __restrict__ dq, size
   if (i >= n4) return;
   const float4 x = reinterpret_cast<const float4*>(dq_acc)[i];
   if constexpr (sizeof(T) == 2) {
-    bf16x4 y;
-    y[0] = (bf16)(x.x * scale);
-    y[1] = (bf16)(x.y * scale);
-    y[2] = (bf16)(x.z * scale);
-    y[3] = (bf16)(x.w * scale);
+    const bf16x4 y = {(bf16)(x.x * scale), (bf16)(x.y * scale), (bf16)(x.z * scale), (bf16)(x.w * scale)};
     reinterpret_cast<bf16x4*>(dq)[i] = y;
   } else {
     reinterpret_cast<float4*>(dq)[i] = make_float4(x.x * scale, x.y * scale, x.z * scale, x.w * scale);
@@ -374,7 +336,7 @@ void fa_bwd_dq_kernel(const float* __restrict__ dq_acc, T* __restrict__ dq, size
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
-  using L = BwdSmem<T, D>;
+  using C = BwdCfg<T, D>;
   const int BH = a.B * a.H;
   const size_t rows = (size_t)BH * a.N;
   if (stages & kStagePre) {
@@ -388,13 +350,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   if (stages & kStageMain) {
     auto kern = fa_bwd_main_kernel<T, D, CAUSAL>;
     static const hipError_t attr_err =
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::BYTES);
     if (attr_err != hipSuccess) return attr_err;
     const int n_ktiles = (a.N + kBwdBK - 1) / kBwdBK;
-    hipLaunchKernelGGL(kern, dim3(n_ktiles * BH), dim3(kBwdThreads), L::BYTES, stream,
+    hipLaunchKernelGGL(kern, dim3(n_ktiles * BH), dim3(kBwdThreads), C::BYTES, stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        static_cast<const T*>(a.dout), a.lse, a.dsum, a.dq_acc, static_cast<T*>(a.dk),
-                       static_cast<T*>(a.dv), a.N, BH, a.scale, a.scale * kLog2e);
+                       static_cast<T*>(a.dv), a.N, BH, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -10,6 +10,13 @@
 //     row acc_row(i, g) = 8*(i/4) + 4*g + (i%4), column l % 32.
 // bf16 uses v_mfma_f32_32x32x16_bf16 (KPL = 8); fp32 uses
 // v_mfma_f32_32x32x2_f32 (KPL = 1).  Accumulation is always fp32.
+//
+// Memory: every global access goes through a buffer resource that covers
+// exactly one head's tensor, so rows past the end read as zero and writes
+// past the end are dropped by the hardware range check -- no per-element
+// branches.  K/V (forward) and Q/dO (backward) tiles move global -> LDS with
+// buffer_load ... lds (no register staging) into row-major tiles whose
+// 16-byte chunks are XOR-swizzled per row (see Tile below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,9 +29,25 @@ typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+// Smallest exponent factor used: keeps masked scores (-inf) at -inf after the
+// scaling even for scale = 0, while every finite score times it rounds to 0.
+constexpr float kMinFactor = 0x1p-100f;
+
+// Raw buffer resource over [base, base + bytes): gfx9 "raw" descriptor
+// (stride 0, 32-bit data format word), range-checked per access.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 template <typename T> struct Mfma;
 
@@ -35,10 +58,14 @@ template <> struct Mfma<bf16> {
   __device__ __forceinline__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  __device__ __forceinline__ static Frag zero() { return Frag{}; }
-  // 8 consecutive elements (16 bytes) from global or LDS memory
-  __device__ __forceinline__ static Frag load(const bf16* p) { return *reinterpret_cast<const Frag*>(p); }
-  // registers i = KPL*t .. KPL*t+KPL-1 of an accumulator, rounded to bf16
+  // KPL consecutive elements at byte offset `off` of a buffer (16 bytes)
+  __device__ __forceinline__ static Frag load(rsrc_t r, int off) {
+    return __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+  __device__ __forceinline__ static Frag lds(const lds_u8* p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) Frag*>(p);
+  }
+  // registers i = KPL*t .. KPL*t+KPL-1 of an accumulator, rounded to bf16 (RNE)
   __device__ __forceinline__ static Frag pack(const f32x16& x, int t) {
     Frag f;
 #pragma unroll
@@ -54,13 +81,98 @@ template <> struct Mfma<float> {
   __device__ __forceinline__ static f32x16 mma(Frag a, Frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
-  __device__ __forceinline__ static Frag zero() { return 0.f; }
-  __device__ __forceinline__ static Frag load(const float* p) { return *p; }
+  __device__ __forceinline__ static Frag load(rsrc_t r, int off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  }
+  __device__ __forceinline__ static Frag lds(const lds_u8* p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) float*>(p);
+  }
   __device__ __forceinline__ static Frag pack(const f32x16& x, int t) { return x[t]; }
 };
 
 // Row of accumulator register i for lane group g (see the header comment).
 __device__ __forceinline__ constexpr int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
+
+// Row-major LDS tile of D elements per row, R = D*sizeof(T) bytes per row,
+// no padding.  For bf16 the 16-byte chunk c of row r is stored at chunk
+// c ^ swz(r).  The swizzle makes both access patterns conflict-free:
+//   * 16 lanes reading one 16-byte chunk each from 16 consecutive rows
+//     (MFMA operand fragments, ds_read_b128), and
+//   * the transpose read ds_read_b64_tr_b16, where 32 lanes read 8 bytes each
+//     from rows r0..r0+3 (r0 % 4 == 0) and 4 consecutive chunks.
+// With 256-byte rows (d = 128) a row spans all 64 banks, so only the chunk
+// index matters; with 128-byte rows (d = 64) rows of one parity share a half
+// of the banks.  fp32 tiles are not swizzled.
+template <typename T, int D> struct Tile {
+  static constexpr int R = D * (int)sizeof(T);
+  __device__ __forceinline__ static constexpr int swz(int row) {
+    if constexpr (sizeof(T) != 2) return 0;
+    else if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  }
+  // byte offset of element (row, col); col * sizeof(T) must not straddle a chunk
+  __device__ __forceinline__ static constexpr int off(int row, int col) {
+    const int b = col * (int)sizeof(T);
+    return row * R + (((b >> 4) ^ swz(row)) << 4) + (b & 15);
+  }
+};
+
+// One global -> LDS transfer per lane: `bytes` (4 or 16) from byte offset
+// `voff` of buffer `src` to dst + lane*bytes (dst wave-uniform).  Kept out of
+// templates: the host pass rejects this builtin with dependent arguments.
+__device__ __forceinline__ void lds_dma16(rsrc_t src, lds_u8* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(rsrc_t src, lds_u8* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)dst, 4, voff, 0, 0, 0);
+}
+
+// Copy rows [row0, row0 + ROWS) of one head's [N, D] tensor (buffer `src`)
+// into an LDS tile, spread over NW waves: each wave moves 1 KiB per
+// instruction, lane i landing at byte 16*i of the wave's segment.  Rows past
+// the end of the tensor read as zero.  Completion is tracked by vmcnt.
+template <typename T, int D, int ROWS, int NW>
+__device__ __forceinline__ void tile_to_lds(rsrc_t src, lds_u8* tile, int row0, int w, int lane) {
+  using G = Tile<T, D>;
+  constexpr int SEGS = ROWS * G::R / 1024;
+  static_assert(SEGS % NW == 0, "tile must split evenly over the waves");
+#pragma unroll
+  for (int r = 0; r < SEGS / NW; ++r) {
+    const int s = w * (SEGS / NW) + r;
+    const int o = s * 1024 + lane * 16;
+    const int row = o / G::R;
+    const int chunk = ((o % G::R) >> 4) ^ G::swz(row);
+    lds_dma16(src, tile + s * 1024, (row0 + row) * G::R + chunk * 16);
+  }
+}
+
+// fp32 atomic add at byte offset `voff` of a buffer (dropped past its end).
+__device__ __forceinline__ void atomic_add_f32(rsrc_t r, int voff, float v) {
+  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, voff, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposed bf16 A fragment (M = columns, K = rows) from a swizzled tile:
+// lane l gets column col0 + l%32 of rows row0 + 8a + 4g + b (a in {0,1},
+// b in 0..3) -- the rows that accumulator registers 8t..8t+7 of lane group g
+// hold for a 32-row block when row0 = 16t.  Two ds_read_b64_tr_b16: within
+// each 16-lane group the instruction hands output lane 4p+q element e of
+// input lane 4e+p's 4-element read (element q), i.e. a 4x16 transpose.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_tr_frag(const lds_u8* tile, int row0, int col0, int lane) {
+  using G = Tile<bf16, D>;
+  const int j = lane & 15;
+  const int h = (lane >> 4) & 1;
+  const int g = lane >> 5;
+  const int row = row0 + 4 * g + (j >> 2);
+  const int col = col0 + 16 * h + 4 * (j & 3);
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  union { s16x4 s[2]; bf16x8 b; } u;
+  u.s[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + G::off(row, col)));
+  u.s[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + G::off(row + 8, col)));
+  return u.b;
+}
 
 // Both lanes l and l^32 receive f(x[l & 31], x[(l & 31) + 32]) with the
 // operands in the same order, so the two halves of a wave agree bit for bit.
@@ -79,27 +191,36 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // folded into one FMA and the hardware v_exp_f32.  fp32 inputs: base e with
 // the accurate expf, so that the fp32 path keeps about 1e-7 relative error
 // in every probability (the fp32 tolerance is 1e-5 absolute).
+// kLazy: the running max used as the exponent shift is only raised when a
+// new score exceeds it by more than this (in the domain's units), so the
+// un-normalised probabilities stay <= 2^8 and the output accumulator is
+// rescaled only on those rare tiles.
 template <typename T> struct ExpDomain;
 template <> struct ExpDomain<bf16> {
-  __device__ __forceinline__ static float factor(float scale, float scale_log2) { return scale_log2; }
+  static constexpr float kLazy = 8.0f;
+  static constexpr float kToNat = kLn2;          // shift (log2 units) -> natural-log units
+  __device__ __forceinline__ static float factor(float scale) { return fmaxf(scale * kLog2e, kMinFactor); }
   __device__ __forceinline__ static float ex(float x) { return fast_exp2(x); }
   __device__ __forceinline__ static float from_lse(float lse) { return lse * kLog2e; }
 };
 template <> struct ExpDomain<float> {
-  __device__ __forceinline__ static float factor(float scale, float) { return scale; }
+  static constexpr float kLazy = 8.0f * kLn2;
+  static constexpr float kToNat = 1.0f;
+  __device__ __forceinline__ static float factor(float scale) { return fmaxf(scale, kMinFactor); }
   __device__ __forceinline__ static float ex(float x) { return expf(x); }
   __device__ __forceinline__ static float from_lse(float lse) { return lse; }
 };
 
-// 16-byte vector of elements, used for coalesced global<->LDS staging.
-template <typename T> struct Vec16 {
-  static constexpr int N = 16 / sizeof(T);
-  uint4 raw;
-  __device__ __forceinline__ T get(int e) const {
-    union { uint4 u; T t[N]; } c;
-    c.u = raw;
-    return c.t[e];
+// Store 4 consecutive fp32 values, rounded to T, at byte offset `off` of a buffer.
+template <typename T>
+__device__ __forceinline__ void store4(rsrc_t r, int off, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
+  } else {
+    f32x4 v = {a, b, c, d};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
   }
-};
+}
 
 }  // namespace fa
