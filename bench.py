@@ -3,7 +3,7 @@
 
 One step = one pass of the whole path over one batch of synthetic input:
 fa_forward (O, lse) then the backward's three stages (D = rowsum(dO o O),
-the key-block accumulation of dK, dV and dQ, and the dQ conversion), on the
+the key-parallel dK/dV kernel and the query-parallel dQ kernel), on the
 long-context causal problem B=1, H=32, N=16384, d=128, bf16 (fp32
 accumulation).  Inputs are resident in HBM before timing starts.
 
@@ -94,23 +94,24 @@ class Step:
                                                  self.p.N, self.p.d, self.dt, self.ws.data_ptr(),
                                                  self.ws_bytes, self.stream), "fa_backward_preprocess")
 
-    def bwd_main(self):
+    def bwd_dkdv(self):
         p = self
-        self._ck(self.lib.fa_backward_accumulate(p.q.data_ptr(), p.k.data_ptr(), p.v.data_ptr(),
-                                                 p.do.data_ptr(), p.lse.data_ptr(), p.dk.data_ptr(),
-                                                 p.dv.data_ptr(), self.p.B, self.p.H, self.p.N, self.p.d,
-                                                 int(self.p.causal), self.p.scale, self.dt, p.ws.data_ptr(),
-                                                 self.ws_bytes, self.stream), "fa_backward_accumulate")
+        self._ck(self.lib.fa_backward_dkdv(p.q.data_ptr(), p.k.data_ptr(), p.v.data_ptr(), p.do.data_ptr(),
+                                           p.lse.data_ptr(), p.dk.data_ptr(), p.dv.data_ptr(), self.p.B, self.p.H,
+                                           self.p.N, self.p.d, int(self.p.causal), self.p.scale, self.dt,
+                                           p.ws.data_ptr(), self.ws_bytes, self.stream), "fa_backward_dkdv")
 
-    def bwd_final(self):
-        self._ck(self.lib.fa_backward_finalize(self.dq.data_ptr(), self.p.B, self.p.H, self.p.N, self.p.d,
-                                               self.p.scale, self.dt, self.ws.data_ptr(), self.ws_bytes,
-                                               self.stream), "fa_backward_finalize")
+    def bwd_dq(self):
+        p = self
+        self._ck(self.lib.fa_backward_dq(p.q.data_ptr(), p.k.data_ptr(), p.v.data_ptr(), p.do.data_ptr(),
+                                         p.lse.data_ptr(), p.dq.data_ptr(), self.p.B, self.p.H, self.p.N, self.p.d,
+                                         int(self.p.causal), self.p.scale, self.dt, p.ws.data_ptr(), self.ws_bytes,
+                                         self.stream), "fa_backward_dq")
 
-    STAGES = ("fwd", "bwd_pre", "bwd_main", "bwd_final")
+    STAGES = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
 
     def run(self, events=None):
-        fns = (self.forward, self.bwd_pre, self.bwd_main, self.bwd_final)
+        fns = (self.forward, self.bwd_pre, self.bwd_dkdv, self.bwd_dq)
         if events is None:
             for fn in fns:
                 fn()
@@ -138,24 +139,29 @@ def time_steps(step, torch, steps, warmup):
 
 
 def kernel_table(p, avg):
+    """Per-kernel time and throughput.  FLOPs per launch follow the stated
+    convention split by products: the backward's 2.5x-forward budget is five
+    N x N x d products; dK/dV performs four of them (S, dP, dV, dK) and dQ
+    three (S, dP, dQ) -- S and dP are recomputed in both, so the two kernels
+    together execute 7/5 of the convention's backward FLOPs."""
     fwd_f, bwd_f = p.fwd_flops(), p.bwd_flops()
+    unit = bwd_f / 5.0                       # one N x N x d product (halved when causal)
     elt = 2 if p.dtype == "bf16" else 4
     rows = p.B * p.H * p.N
     tens = rows * p.d * elt
     out = {}
-    out["fwd"] = {"kernel": "fa_fwd_kernel", "ms": avg["fwd"], "flops": fwd_f,
-                  "tflops": fwd_f / avg["fwd"] * 1e-9, "frac_peak": fwd_f / avg["fwd"] * 1e-9 / PEAK_BF16_TFLOPS}
-    out["bwd_main"] = {"kernel": "fa_bwd_main_kernel", "ms": avg["bwd_main"], "flops": bwd_f,
-                       "tflops": bwd_f / avg["bwd_main"] * 1e-9,
-                       "frac_peak": bwd_f / avg["bwd_main"] * 1e-9 / PEAK_BF16_TFLOPS}
-    # memory-bound helpers: algorithmic bytes = each operand touched once
-    pre_bytes = 2 * tens + rows * 4 + rows * p.d * 4           # read O, dO; write D, zero dQ_acc
-    fin_bytes = rows * p.d * 4 + tens                          # read dQ_acc, write dQ
+
+    def mm(name, kernel, flops):
+        out[name] = {"kernel": kernel, "ms": avg[name], "flops": flops, "tflops": flops / avg[name] * 1e-9,
+                     "frac_peak": flops / avg[name] * 1e-9 / PEAK_BF16_TFLOPS}
+
+    mm("fwd", "fa_fwd_kernel", fwd_f)
+    mm("bwd_dkdv", "fa_bwd_dkdv_kernel", 4 * unit)
+    mm("bwd_dq", "fa_bwd_dq_kernel", 3 * unit)
+    pre_bytes = 2 * tens + rows * 4                            # read O, dO; write D
     out["bwd_pre"] = {"kernel": "fa_bwd_pre_kernel", "ms": avg["bwd_pre"], "bytes": pre_bytes,
                       "gbs": pre_bytes / avg["bwd_pre"] * 1e-6}
-    out["bwd_final"] = {"kernel": "fa_bwd_dq_kernel", "ms": avg["bwd_final"], "bytes": fin_bytes,
-                        "gbs": fin_bytes / avg["bwd_final"] * 1e-6}
-    out["bwd_total"] = {"ms": avg["bwd_pre"] + avg["bwd_main"] + avg["bwd_final"]}
+    out["bwd_total"] = {"ms": avg["bwd_pre"] + avg["bwd_dkdv"] + avg["bwd_dq"]}
     out["bwd_total"]["tflops"] = bwd_f / out["bwd_total"]["ms"] * 1e-9
     out["bwd_total"]["frac_peak"] = out["bwd_total"]["tflops"] / PEAK_BF16_TFLOPS
     return out
@@ -238,7 +244,7 @@ def main(argv=None):
 
     total_flops = p.fwd_flops() + p.bwd_flops()
     value = total_flops / ms_step * 1e-9
-    dom = max(("fwd", "bwd_main"), key=lambda k: kt[k]["ms"])
+    dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda k: kt[k]["ms"])
     traffic = measured_traffic(kt[dom]["kernel"])
     roofline = {"bound": "mfma", "kernel": kt[dom]["kernel"], "achieved": kt[dom]["tflops"],
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": kt[dom]["tflops"] / PEAK_BF16_TFLOPS,

@@ -83,9 +83,8 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace that fa_backward needs: the fp32 row terms
- * D = rowsum(dO o O) ([B,H,N]) and an fp32 dQ accumulator ([B,H,N,d]),
- * each 256-byte aligned.  Linear in N: no N x N buffer is ever used.
- * Returns 0 for invalid or empty shapes.
+ * D = rowsum(dO o O) ([B,H,N]), 256-byte aligned.  Linear in N: no N x N
+ * buffer is ever used.  Returns 0 for invalid or empty shapes.
  */
 size_t fa_backward_workspace_size(int B, int H, int N, int d);
 
@@ -96,8 +95,7 @@ size_t fa_backward_workspace_size(int B, int H, int N, int d);
  * least fa_backward_workspace_size(B,H,N,d) bytes, 256-byte aligned; its
  * contents on entry are ignored and on exit are unspecified.  P is
  * recomputed as exp(scale * Q K^T - lse) ("Как работает FlashAttention
- * математически" section 5); dQ is accumulated in fp32 in the workspace and
- * converted at the end, so dQ may differ between runs in the last bits.
+ * математически" section 5).  The result is deterministic (no atomics).
  */
 int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
@@ -107,23 +105,26 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
 /*
  * The three stages that fa_backward enqueues, in order, for callers that
  * schedule or time them separately.  Same arguments, layout and workspace
- * as fa_backward; calling the three in order on one stream is exactly
- * fa_backward.
+ * as fa_backward; calling fa_backward_preprocess and then the other two (in
+ * either order, both after it) on one stream is exactly fa_backward.
  *   fa_backward_preprocess: D_i = do_i . o_i (fp32, the row term of the
  *     softmax Jacobian, "Overview of Flash Attention series", Backward Pass)
- *     into the workspace, and zero the workspace's fp32 dQ accumulator.
- *   fa_backward_accumulate: recompute S and P from lse key block by key
- *     block, write dK and dV, and add (dS K) into the dQ accumulator.
- *   fa_backward_finalize: dQ = scale * accumulator, rounded to dtype.
+ *     into the workspace.
+ *   fa_backward_dkdv: recompute S and P from lse key block by key block and
+ *     write dK = scale * dS^T Q and dV = P^T dO.
+ *   fa_backward_dq: recompute them query block by query block and write
+ *     dQ = scale * dS K.
  */
 int fa_backward_preprocess(const void* o, const void* dout, int B, int H, int N, int d, int dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
-int fa_backward_accumulate(const void* q, const void* k, const void* v, const void* dout,
-                           const float* lse, void* dk, void* dv, int B, int H, int N, int d,
-                           int causal, float scale, int dtype, void* workspace,
-                           size_t workspace_bytes, void* stream);
-int fa_backward_finalize(void* dq, int B, int H, int N, int d, float scale, int dtype,
-                         void* workspace, size_t workspace_bytes, void* stream);
+int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                     const float* lse, void* dk, void* dv, int B, int H, int N, int d,
+                     int causal, float scale, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+int fa_backward_dq(const void* q, const void* k, const void* v, const void* dout,
+                   const float* lse, void* dq, int B, int H, int N, int d, int causal,
+                   float scale, int dtype, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 /* Static English description of an fa_status value (never NULL). */
 const char* fa_strerror(int status);

@@ -15,12 +15,12 @@ import math
 from typing import Optional, Tuple
 
 from . import _lib
-from ._lib import (FA_BF16, FA_F32, FaError, fa_backward, fa_backward_accumulate, fa_backward_finalize,
+from ._lib import (FA_BF16, FA_F32, FaError, fa_backward, fa_backward_dkdv, fa_backward_dq,
                    fa_backward_preprocess, fa_backward_workspace_size, fa_forward, fa_strerror)
 
 __all__ = ["forward", "backward", "workspace_size", "FaError", "FA_F32", "FA_BF16",
            "fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_preprocess",
-           "fa_backward_accumulate", "fa_backward_finalize", "fa_strerror", "load_library",
+           "fa_backward_dkdv", "fa_backward_dq", "fa_strerror", "load_library",
            "backward_stages"]
 
 
@@ -113,7 +113,8 @@ def backward(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] =
 
 def backward_stages(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
                     dq=None, dk=None, dv=None, workspace=None):
-    """The same result as :func:`backward`, through the three staged entry points."""
+    """The same result as :func:`backward`, through the three staged entry points
+    (dQ before dK/dV here, to exercise the documented freedom of order)."""
     import torch
     B, H, N, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
@@ -131,11 +132,12 @@ def backward_stages(q, k, v, o, do, lse, causal: bool = False, scale: Optional[f
     st = fa_backward_preprocess(o.data_ptr(), do.data_ptr(), B, H, N, d, dt, ws, wn, s)
     if st != 0:
         raise FaError(st, "fa_backward_preprocess")
-    st = fa_backward_accumulate(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                                dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale, dt, ws, wn, s)
+    st = fa_backward_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                        dq.data_ptr(), B, H, N, d, causal, scale, dt, ws, wn, s)
     if st != 0:
-        raise FaError(st, "fa_backward_accumulate")
-    st = fa_backward_finalize(dq.data_ptr(), B, H, N, d, scale, dt, ws, wn, s)
+        raise FaError(st, "fa_backward_dq")
+    st = fa_backward_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                          dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale, dt, ws, wn, s)
     if st != 0:
-        raise FaError(st, "fa_backward_finalize")
+        raise FaError(st, "fa_backward_dkdv")
     return dq, dk, dv

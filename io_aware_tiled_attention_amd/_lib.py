@@ -21,7 +21,7 @@ STATUS = {
     5: "FA_ERR_SCALE", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ALIGN",
 }
 EXPORTED = ("fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_preprocess",
-            "fa_backward_accumulate", "fa_backward_finalize", "fa_strerror")
+            "fa_backward_dkdv", "fa_backward_dq", "fa_strerror")
 
 _lock = threading.Lock()
 _lib = None
@@ -55,10 +55,10 @@ def load() -> ctypes.CDLL:
         lib.fa_backward_workspace_size.restype = sz
         lib.fa_backward_preprocess.argtypes = [vp, vp, i, i, i, i, i, vp, sz, vp]
         lib.fa_backward_preprocess.restype = i
-        lib.fa_backward_accumulate.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
-        lib.fa_backward_accumulate.restype = i
-        lib.fa_backward_finalize.argtypes = [vp, i, i, i, i, f, i, vp, sz, vp]
-        lib.fa_backward_finalize.restype = i
+        lib.fa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+        lib.fa_backward_dkdv.restype = i
+        lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+        lib.fa_backward_dq.restype = i
         lib.fa_strerror.argtypes = [i]
         lib.fa_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -79,15 +79,16 @@ def fa_backward_preprocess(o, dout, B, H, N, d, dtype, workspace, workspace_byte
     return load().fa_backward_preprocess(o, dout, B, H, N, d, dtype, workspace, workspace_bytes, stream)
 
 
-def fa_backward_accumulate(q, k, v, dout, lse, dk, dv, B, H, N, d, causal, scale, dtype,
-                           workspace, workspace_bytes, stream) -> int:
-    return load().fa_backward_accumulate(q, k, v, dout, lse, dk, dv, B, H, N, d, int(causal),
-                                         float(scale), dtype, workspace, workspace_bytes, stream)
+def fa_backward_dkdv(q, k, v, dout, lse, dk, dv, B, H, N, d, causal, scale, dtype,
+                     workspace, workspace_bytes, stream) -> int:
+    return load().fa_backward_dkdv(q, k, v, dout, lse, dk, dv, B, H, N, d, int(causal),
+                                   float(scale), dtype, workspace, workspace_bytes, stream)
 
 
-def fa_backward_finalize(dq, B, H, N, d, scale, dtype, workspace, workspace_bytes, stream) -> int:
-    return load().fa_backward_finalize(dq, B, H, N, d, float(scale), dtype, workspace,
-                                       workspace_bytes, stream)
+def fa_backward_dq(q, k, v, dout, lse, dq, B, H, N, d, causal, scale, dtype,
+                   workspace, workspace_bytes, stream) -> int:
+    return load().fa_backward_dq(q, k, v, dout, lse, dq, B, H, N, d, int(causal), float(scale),
+                                 dtype, workspace, workspace_bytes, stream)
 
 
 def fa_backward_workspace_size(B, H, N, d) -> int:

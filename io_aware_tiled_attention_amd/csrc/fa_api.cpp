@@ -42,30 +42,31 @@ int run_backward(int stages, const void* q, const void* k, const void* v, const 
   const int st = check_shape(B, H, N, d, dtype, scale, &empty);
   if (st != FA_OK) return st;
   if (empty) return FA_OK;
-  const bool pre = stages & fa::kStagePre, mid = stages & fa::kStageMain, fin = stages & fa::kStageFinal;
-  const void* need[9];
+  const bool pre = stages & fa::kStagePre, kv = stages & fa::kStageDkDv, dqs = stages & fa::kStageDq;
+  const void* need[12];
   int n_need = 0;
   if (pre) {
     need[n_need++] = o;
     need[n_need++] = dout;
   }
-  if (mid) {
-    const void* ptrs[] = {q, k, v, lse, dk, dv};
+  if (kv || dqs) {
+    const void* ptrs[] = {q, k, v, dout, lse};
     for (const void* p : ptrs) need[n_need++] = p;
-    if (!pre) need[n_need++] = dout;
   }
-  if (fin) need[n_need++] = dq;
+  if (kv) {
+    need[n_need++] = dk;
+    need[n_need++] = dv;
+  }
+  if (dqs) need[n_need++] = dq;
   for (int i = 0; i < n_need; ++i)
     if (!need[i]) return FA_ERR_NULL;
   for (int i = 0; i < n_need; ++i)
     if (!aligned16(need[i])) return FA_ERR_ALIGN;
   const size_t rows = (size_t)B * H * N;
-  const size_t bytes = fa::ws_dsum_bytes(rows) + fa::ws_dq_bytes(rows, (size_t)d);
-  if (!workspace || workspace_bytes < bytes) return FA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < fa::ws_dsum_bytes(rows)) return FA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_ALIGN;
-  char* ws = static_cast<char*>(workspace);
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal ? 1 : 0, dtype, scale,
-                reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + fa::ws_dsum_bytes(rows))};
+                static_cast<float*>(workspace)};
   return hip_status(fa::launch_backward(a, stages, static_cast<hipStream_t>(stream)));
 }
 
@@ -88,34 +89,34 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
   bool empty = false;
   if (check_shape(B, H, N, d, FA_BF16, 1.f, &empty) != FA_OK || empty) return 0;
-  const size_t rows = (size_t)B * H * N;
-  return fa::ws_dsum_bytes(rows) + fa::ws_dq_bytes(rows, (size_t)d);
+  return fa::ws_dsum_bytes((size_t)B * H * N);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal,
                 float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return run_backward(fa::kStagePre | fa::kStageMain | fa::kStageFinal, q, k, v, o, dout, lse, dq, dk, dv, B,
-                      H, N, d, causal, scale, dtype, workspace, workspace_bytes, stream);
+  return run_backward(fa::kStagePre | fa::kStageDkDv | fa::kStageDq, q, k, v, o, dout, lse, dq, dk, dv, B, H, N,
+                      d, causal, scale, dtype, workspace, workspace_bytes, stream);
 }
 
 int fa_backward_preprocess(const void* o, const void* dout, int B, int H, int N, int d, int dtype,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  return run_backward(fa::kStagePre, nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr, nullptr,
-                      B, H, N, d, 0, 1.f, dtype, workspace, workspace_bytes, stream);
+  return run_backward(fa::kStagePre, nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr, nullptr, B, H,
+                      N, d, 0, 1.f, dtype, workspace, workspace_bytes, stream);
 }
 
-int fa_backward_accumulate(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                           void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, int dtype,
-                           void* workspace, size_t workspace_bytes, void* stream) {
-  return run_backward(fa::kStageMain, q, k, v, nullptr, dout, lse, nullptr, dk, dv, B, H, N, d, causal, scale,
+int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk,
+                     void* dv, int B, int H, int N, int d, int causal, float scale, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return run_backward(fa::kStageDkDv, q, k, v, nullptr, dout, lse, nullptr, dk, dv, B, H, N, d, causal, scale,
                       dtype, workspace, workspace_bytes, stream);
 }
 
-int fa_backward_finalize(void* dq, int B, int H, int N, int d, float scale, int dtype, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-  return run_backward(fa::kStageFinal, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dq, nullptr,
-                      nullptr, B, H, N, d, 0, scale, dtype, workspace, workspace_bytes, stream);
+int fa_backward_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dq,
+                   int B, int H, int N, int d, int causal, float scale, int dtype, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return run_backward(fa::kStageDq, q, k, v, nullptr, dout, lse, dq, nullptr, nullptr, B, H, N, d, causal, scale,
+                      dtype, workspace, workspace_bytes, stream);
 }
 
 const char* fa_strerror(int status) {

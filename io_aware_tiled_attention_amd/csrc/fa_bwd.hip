@@ -8,31 +8,31 @@
 //   D_i = do_i . o_i                         (the row term of the softmax Jacobian)
 //   dS  = P o (dP - D)
 //   dQ  = scale * dS K,   dK = scale * dS^T Q
-// The N x N matrices P, dP and dS exist only tile by tile in registers and
-// LDS; only the O(N) statistics lse and D are read from memory ("Как работает
+// The N x N matrices P, dP and dS exist only tile by tile in registers; only
+// the O(N) statistics lse and D are read from memory ("Как работает
 // FlashAttention математически" section 5: recompute instead of store).
 //
-// Three launches on the caller's stream:
-//   1. fa_bwd_pre: D_i = rowsum(dO o O) in fp32, and zero the fp32 dQ
-//      accumulator (a plain store kernel, so the sequence is graph-capturable).
-//   2. fa_bwd_main: a workgroup owns 128 keys (4 waves x 32) and keeps its
+// Three launches on the caller's stream, none of them with atomics:
+//   1. fa_bwd_pre: D_i = rowsum(dO o O) in fp32 into the workspace.
+//   2. fa_bwd_dkdv: a workgroup owns 128 keys (4 waves x 32) and keeps its
 //      slice of K, V and the fp32 accumulators dK^T, dV^T in registers while
 //      sweeping the query blocks that can see them (all blocks, or the blocks
-//      at or below the diagonal when causal), BQ query rows at a time.  Per
-//      32-row sub-block each wave recomputes S and P for its 32 keys, forms dP
-//      and dS, and accumulates dV^T += dO^T P and dK^T += Q^T dS on the matrix
-//      cores (P and dS are already in B-operand layout; dO^T and Q^T come from
-//      the row-major LDS tiles through the gfx950 transpose read).  dS^T goes
-//      to LDS; in the next iteration each wave reads it back, transposed, as
-//      the A operand of dQ = dS K over all 128 keys and adds its tiles to the
-//      fp32 accumulator with buffer atomics -- one contribution per (query
-//      block, workgroup), one barrier per query block.
-//      Query blocks are swept from the last one downwards: all key tiles of a
-//      head run at the same time on one XCD and reach the same query block
-//      together, so their dQ atomics meet in that XCD's L2.
-//   3. fa_bwd_dq: dQ = scale * accumulator, rounded to the element type.
-// The loop order over (key block outer, query block inner) is the one whose
-// dK/dV stay on chip; the pages leave the backward loop order open.
+//      at or below the diagonal when causal), BQ query rows at a time through
+//      double-buffered LDS.  Per 32-row sub-block each wave recomputes S and P
+//      for its 32 keys, forms dP and dS, and accumulates dV^T += dO^T P and
+//      dK^T += Q^T dS on the matrix cores: P and dS are already in B-operand
+//      layout, dO^T and Q^T come from the row-major LDS tiles through the
+//      gfx950 transpose read.
+//   3. fa_bwd_dq: the same recomputation in the transposed orientation, one
+//      workgroup per 128 query rows (like the forward): S^T = K Q^T and
+//      dP^T = V dO^T leave each lane with one query's scores, lse and D are
+//      per-lane scalars, and dQ^T += K^T dS^T takes dS^T straight from
+//      registers (K^T from the K tile through the transpose read).  dQ is
+//      written once.
+// Splitting dQ from dK/dV costs the two products S and dP a second time but
+// needs no cross-workgroup reduction: on this GPU fp32 atomics are executed at
+// the memory side, and the fused form spent most of its time waiting on them.
+// The pages leave the backward loop order open (their figure is missing).
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -50,28 +50,20 @@ struct BwdCfg {
   static constexpr int BQ = ESZ == 2 ? 64 : 32;        // query rows per block
   static constexpr int QB = BQ / 32;                   // 32-row sub-blocks
   static constexpr int NDB = D / 32;                   // 32-wide d blocks
-  static constexpr int NDQ = NDB * QB;                 // 32x32 dQ tiles per block
-  static constexpr int TPW = (NDQ + kBwdWaves - 1) / kBwdWaves;   // dQ tiles per wave
   static constexpr int QTILE = BQ * D * ESZ;           // bytes of the Q (or dO) tile
   static constexpr int STATS = 2 * 64 * 4;             // lse, D: 64 floats each
   static constexpr int STAGE = 2 * QTILE + STATS;
-  static constexpr int DST = kBwdBK * BQ * ESZ;        // dS^T tile [keys][queries]
-  static constexpr int BYTES = 2 * STAGE + 2 * DST;
-  static_assert(ESZ != 2 || kBwdBK * D * ESZ <= 2 * DST, "K staging fits in the dS^T buffers");
-  static_assert(NDB % 1 == 0 && (NDQ <= kBwdWaves || NDQ % kBwdWaves == 0), "dQ tiles split over waves");
-  static_assert(kBwdWaves % NDB == 0 || NDB % kBwdWaves == 0, "one d block per wave");
+  static constexpr int BYTES = 2 * STAGE;
   __device__ static lds_u8* q(lds_u8* b, int st) { return b + st * STAGE; }
   __device__ static lds_u8* dout(lds_u8* b, int st) { return b + st * STAGE + QTILE; }
   __device__ static lds_u8* lse(lds_u8* b, int st) { return b + st * STAGE + 2 * QTILE; }
   __device__ static lds_u8* dd(lds_u8* b, int st) { return b + st * STAGE + 2 * QTILE + 256; }
-  __device__ static lds_u8* dst(lds_u8* b, int k) { return b + 2 * STAGE + k * DST; }
 };
 
 // ---------------------------------------------------------------- 1. preprocess
 template <typename T, int D>
 __global__ __launch_bounds__(256)
-void fa_bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __restrict__ dsum,
-                       float* __restrict__ dq_acc, size_t rows) {
+void fa_bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __restrict__ dsum, size_t rows) {
   constexpr int VE = 16 / sizeof(T);
   constexpr int CPR = D / VE;                 // threads per row
   constexpr int RPB = 256 / CPR;              // rows per block
@@ -85,31 +77,24 @@ void fa_bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, float*
     d.u = *reinterpret_cast<const uint4*>(dO + row * D + col);
 #pragma unroll
     for (int e = 0; e < VE; ++e) part += (float)o.t[e] * (float)d.t[e];
-    float4* z = reinterpret_cast<float4*>(dq_acc + row * D + col);
-#pragma unroll
-    for (int e = 0; e < VE / 4; ++e) z[e] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int off = CPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
   if (row < rows && tid % CPR == 0) dsum[row] = part;
 }
 
-// ---------------------------------------------------------------- 2. main loop
+// ---------------------------------------------------------------- 2. dK, dV
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 1)
-void fa_bwd_main_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-                        const T* __restrict__ dO, const float* __restrict__ LSE,
-                        const float* __restrict__ dsum, float* __restrict__ dq_acc,
+void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                        const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ dsum,
                         T* __restrict__ dK, T* __restrict__ dV, int N, int BH, float scale) {
   using M = Mfma<T>;
   using C = BwdCfg<T, D>;
-  using G = Tile<T, D>;                 // Q, dO and K tiles: rows x D
-  using GS = Tile<T, C::BQ>;            // dS^T tile: 128 key rows x BQ query columns
+  using G = Tile<T, D>;                 // Q and dO tiles: BQ rows x D
   using X = ExpDomain<T>;
   using Frag = typename M::Frag;
   typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
   constexpr int KPL = M::KPL, KC = M::KC;
   constexpr int NDB = C::NDB, BQ = C::BQ, QB = C::QB;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
@@ -134,7 +119,6 @@ void fa_bwd_main_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
   const rsrc_t rdo = make_rsrc(dO + head, head_bytes);
   const rsrc_t rlse = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
   const rsrc_t rdd = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
-  const rsrc_t rdq = make_rsrc(dq_acc + head, (uint32_t)N * D * 4u);
   const float kfac = X::factor(scale);
 
   // K and V rows of this wave as B operands (column = key, KPL d-values of group g).
@@ -144,26 +128,6 @@ void fa_bwd_main_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
     const int off = mykey * G::R + (c * KC + g * KPL) * (int)sizeof(T);
     kf[c] = M::load(rk, off);
     vf[c] = M::load(rv, off);
-  }
-
-  // K^T for this wave's dQ tiles (column d = dblk*32 + l%32) as the B operand of
-  // dQ = dS K; k-step kc covers keys kc*KC.., in the order of the dS fragments.
-  const int dblk = w % NDB;
-  Frag ktf[kBwdBK / KC];
-  if constexpr (sizeof(T) == 2) {
-    // stage the workgroup's 128 K rows in the (not yet used) dS^T buffers and
-    // read them back transposed: lane gets keys kc*16 + 8a + 4g + b
-    lds_u8* kst = C::dst(smem, 0);
-    tile_to_lds<T, D, kBwdBK, kBwdWaves>(rk, kst, k0, w, lane);
-    wait_vmem();
-    __syncthreads();
-#pragma unroll
-    for (int kc = 0; kc < kBwdBK / KC; ++kc) ktf[kc] = lds_tr_frag<D>(kst, kc * 16, dblk * 32, lane);
-    __syncthreads();
-  } else {
-#pragma unroll
-    for (int kc = 0; kc < kBwdBK / KC; ++kc)
-      ktf[kc] = M::load(rk, (k0 + kc * 2 + g) * G::R + (dblk * 32 + r32) * (int)sizeof(T));
   }
 
   f32x16 dv_acc[NDB], dk_acc[NDB];
@@ -181,67 +145,29 @@ void fa_bwd_main_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
     if (w == 1) lds_dma4(rdd, C::dd(smem, st), (q0b + lane) * 4);
   };
 
-  // dQ tiles of the block whose dS^T is in buffer `buf`: tile t = w + 4u covers
-  // d block t % NDB (= dblk) and query sub-block t / NDB.
-  auto dq_block = [&](int q0b, int buf) {
-    const lds_u8* ds = C::dst(smem, buf);
-#pragma unroll
-    for (int u = 0; u < C::TPW; ++u) {
-      const int t = w + kBwdWaves * u;
-      if (t < C::NDQ) {
-        const int qblk = t / NDB;
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int kc = 0; kc < kBwdBK / KC; ++kc) {
-          Frag a;
-          if constexpr (sizeof(T) == 2) a = lds_tr_frag<BQ>(ds, kc * 16, qblk * 32, lane);
-          else a = M::lds(ds + GS::off(kc * 2 + g, qblk * 32 + r32));
-          acc = M::mma(a, ktf[kc], acc);
-        }
-        // lane holds column d = dblk*32 + r32 of query rows acc_row(i, g)
-        const int qrow = q0b + qblk * 32;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          atomic_add_f32(rdq, ((qrow + acc_row(i, g)) * D + dblk * 32 + r32) * 4, acc[i]);
-      }
-    }
-  };
+  // Query blocks from the first one that sees these keys to the end.
+  const int q_begin = CAUSAL ? k0 : 0;
+  const int nblocks = (N - q_begin + BQ - 1) / BQ;
 
-  // Query blocks from the last one down to the first that sees these keys.
-  const int nqb_total = (N + BQ - 1) / BQ;
-  const int qb_first = CAUSAL ? k0 / BQ : 0;
-  const int nblocks = nqb_total - qb_first;
-  auto block_start = [&](int it) { return (nqb_total - 1 - it) * BQ; };
-
-  load_block(block_start(0), 0);
+  load_block(q_begin, 0);
   wait_vmem();
   __syncthreads();
 
   for (int it = 0; it < nblocks; ++it) {
-    const int q0b = block_start(it);
+    const int q0b = q_begin + it * BQ;
     const int st = it & 1;
-    if (it + 1 < nblocks) load_block(block_start(it + 1), st ^ 1);
-    if (it > 0) dq_block(block_start(it - 1), st ^ 1);
+    if (it + 1 < nblocks) load_block(q0b + BQ, st ^ 1);
 
     const lds_u8* qs = C::q(smem, st);
     const lds_u8* dos = C::dout(smem, st);
     const lds_u8* lse_s = C::lse(smem, st);
     const lds_u8* dd_s = C::dd(smem, st);
-    lds_u8* ds_out = C::dst(smem, st);
 
 #pragma unroll
     for (int qs_i = 0; qs_i < QB; ++qs_i) {
       const int qsb = q0b + qs_i * 32;
-      if (CAUSAL && qsb + 31 < kw0) {
-        // every query of the sub-block precedes every key of the wave: dS = 0
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int off = GS::off(w * kBwdKW + r32, qs_i * 32 + 8 * a + 4 * g);
-          if constexpr (sizeof(T) == 2) *(lds_u32x2*)(ds_out + off) = u32x2{0u, 0u};
-          else *(lds_u32x4*)(ds_out + off) = u32x4{0u, 0u, 0u, 0u};
-        }
-        continue;
-      }
+      // every query of the sub-block precedes every key of the wave: nothing to add
+      if (CAUSAL && qsb + 31 < kw0) continue;
       // S = Q K^T and dP = dO V^T: rows = queries, column = this lane's key.
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -287,23 +213,10 @@ void fa_bwd_main_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
           dk_acc[db] = M::mma(a_q, dsb, dk_acc[db]);
         }
       }
-      // dS^T (row = key, 4 consecutive query columns per store) for the dQ product.
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int off = GS::off(w * kBwdKW + r32, qs_i * 32 + 8 * a + 4 * g);
-        if constexpr (sizeof(T) == 2) {
-          const bf16x4 v4 = {(bf16)dp[4 * a], (bf16)dp[4 * a + 1], (bf16)dp[4 * a + 2], (bf16)dp[4 * a + 3]};
-          *(lds_u32x2*)(ds_out + off) = __builtin_bit_cast(u32x2, v4);
-        } else {
-          const f32x4 v4 = {dp[4 * a], dp[4 * a + 1], dp[4 * a + 2], dp[4 * a + 3]};
-          *(lds_u32x4*)(ds_out + off) = __builtin_bit_cast(u32x4, v4);
-        }
-      }
     }
     wait_vmem();
     __syncthreads();
   }
-  dq_block(block_start(nblocks - 1), (nblocks - 1) & 1);
 
   // dK = scale * dK_acc, dV = dV_acc; lane holds key mykey, d = db*32 + acc_row(i, g).
   const rsrc_t rdk = make_rsrc(dK + head, head_bytes);
@@ -319,52 +232,180 @@ void fa_bwd_main_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
     }
 }
 
-// ---------------------------------------------------------------- 3. dQ finalise
-template <typename T>
-__global__ __launch_bounds__(256)
-void fa_bwd_dq_kernel(const float* __restrict__ dq_acc, T* __restrict__ dq, size_t n4, float scale) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  const float4 x = reinterpret_cast<const float4*>(dq_acc)[i];
-  if constexpr (sizeof(T) == 2) {
-    const bf16x4 y = {(bf16)(x.x * scale), (bf16)(x.y * scale), (bf16)(x.z * scale), (bf16)(x.w * scale)};
-    reinterpret_cast<bf16x4*>(dq)[i] = y;
-  } else {
-    reinterpret_cast<float4*>(dq)[i] = make_float4(x.x * scale, x.y * scale, x.z * scale, x.w * scale);
+// ---------------------------------------------------------------- 3. dQ
+constexpr int kDqWaves = 4;
+constexpr int kDqQW = 32;                       // query rows per wave
+constexpr int kDqBR = kDqWaves * kDqQW;         // query rows per workgroup
+constexpr int kDqBC = 64;                       // keys per K/V tile
+constexpr int kDqThreads = kDqWaves * 64;
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kDqThreads, sizeof(T) == 2 ? 2 : 1)
+void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                      const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ dsum,
+                      T* __restrict__ dQ, int N, int BH, int n_qtiles, float scale) {
+  using M = Mfma<T>;
+  using G = Tile<T, D>;
+  using X = ExpDomain<T>;
+  using Frag = typename M::Frag;
+  constexpr int KPL = M::KPL, KC = M::KC;
+  constexpr int NKB = kDqBC / 32;
+  constexpr int NDB = D / 32;
+  constexpr int TILE = kDqBC * G::R;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
+  lds_u8* smem = (lds_u8*)smem_raw;      // [K st0][K st1][V st0][V st1]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int g = lane >> 5;
+  const int r32 = lane & 31;
+
+  const int bh = blockIdx.x % BH;
+  int qt = blockIdx.x / BH;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;         // longest first
+  const int q0 = qt * kDqBR;
+  const size_t head = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * G::R;
+  const rsrc_t rq = make_rsrc(Q + head, head_bytes);
+  const rsrc_t rk = make_rsrc(K + head, head_bytes);
+  const rsrc_t rv = make_rsrc(V + head, head_bytes);
+  const rsrc_t rdo = make_rsrc(dO + head, head_bytes);
+  const int qw0 = q0 + w * kDqQW;
+  const int myq = qw0 + r32;
+  const float kfac = X::factor(scale);
+
+  // Q^T and dO^T as B operands (column = query, KPL d-values of group g);
+  // this lane's lse (in the exponent domain) and D are scalars.
+  Frag qf[D / KC], dof[D / KC];
+#pragma unroll
+  for (int c = 0; c < D / KC; ++c) {
+    const int off = myq * G::R + (c * KC + g * KPL) * (int)sizeof(T);
+    qf[c] = M::load(rq, off);
+    dof[c] = M::load(rdo, off);
   }
+  const rsrc_t rlse = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
+  const rsrc_t rdd = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
+  const float lse_x = X::from_lse(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rlse, myq * 4, 0, 0)));
+  const float dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdd, myq * 4, 0, 0));
+
+  const int kv_end = CAUSAL ? min(N, q0 + kDqBR) : N;
+  const int ntiles = (kv_end + kDqBC - 1) / kDqBC;
+  const int wave_last = CAUSAL ? min(ntiles - 1, (qw0 + kDqQW - 1) / kDqBC) : ntiles - 1;
+
+  auto load_tile = [&](int j, int st) {
+    tile_to_lds<T, D, kDqBC, kDqWaves>(rk, smem + st * TILE, j * kDqBC, w, lane);
+    tile_to_lds<T, D, kDqBC, kDqWaves>(rv, smem + (2 + st) * TILE, j * kDqBC, w, lane);
+  };
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  load_tile(0, 0);
+  wait_vmem();
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int st = j & 1;
+    const int kv0 = j * kDqBC;
+    if (j + 1 < ntiles) load_tile(j + 1, st ^ 1);
+    if (j <= wave_last) {
+      const lds_u8* ks = smem + st * TILE;
+      const lds_u8* vs = smem + (2 + st) * TILE;
+      // S^T = K Q^T and dP^T = V dO^T: rows = keys, column = this lane's query.
+      f32x16 s[NKB], dp[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
+      }
+#pragma unroll
+      for (int c = 0; c < D / KC; ++c)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int off = G::off(kb * 32 + r32, c * KC + g * KPL);
+          s[kb] = M::mma(M::lds(ks + off), qf[c], s[kb]);
+          dp[kb] = M::mma(M::lds(vs + off), dof[c], dp[kb]);
+        }
+      const bool masked = (CAUSAL && kv0 + kDqBC - 1 > qw0) || (kv0 + kDqBC > N);
+      const int last = CAUSAL ? min(N - 1, myq) : N - 1;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int lim = last - (kv0 + kb * 32 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = X::ex(__builtin_fmaf(s[kb][i], kfac, -lse_x));
+          if (masked) p = (acc_row(i, 0) > lim) ? 0.f : p;
+          dp[kb][i] = p * (dp[kb][i] - dd);
+        }
+      }
+      // dQ^T += K^T dS^T, dS^T straight from registers (B operand), K^T from
+      // the K tile through the transpose read (A operand).
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 32 / KC; ++t) {
+          const Frag dsb = M::pack(dp[kb], t);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            Frag a;
+            if constexpr (sizeof(T) == 2) a = lds_tr_frag<D>(ks, kb * 32 + 16 * t, db * 32, lane);
+            else a = M::lds(ks + G::off(kb * 32 + acc_row(t, g), db * 32 + r32));
+            acc[db] = M::mma(a, dsb, acc[db]);
+          }
+        }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // dQ = scale * acc; lane holds query myq, d = db*32 + acc_row(i, g).
+  const rsrc_t rdq = make_rsrc(dQ + head, head_bytes);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      store4<T>(rdq, myq * G::R + (db * 32 + 8 * a + 4 * g) * (int)sizeof(T), acc[db][4 * a] * scale,
+                acc[db][4 * a + 1] * scale, acc[db][4 * a + 2] * scale, acc[db][4 * a + 3] * scale);
 }
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
-  using C = BwdCfg<T, D>;
   const int BH = a.B * a.H;
   const size_t rows = (size_t)BH * a.N;
   if (stages & kStagePre) {
     constexpr int RPB = 256 / (D / (16 / (int)sizeof(T)));
     const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
     hipLaunchKernelGGL((fa_bwd_pre_kernel<T, D>), grid, dim3(256), 0, stream, static_cast<const T*>(a.o),
-                       static_cast<const T*>(a.dout), a.dsum, a.dq_acc, rows);
+                       static_cast<const T*>(a.dout), a.dsum, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (stages & kStageMain) {
-    auto kern = fa_bwd_main_kernel<T, D, CAUSAL>;
+  if (stages & kStageDkDv) {
+    using C = BwdCfg<T, D>;
+    auto kern = fa_bwd_dkdv_kernel<T, D, CAUSAL>;
     static const hipError_t attr_err =
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::BYTES);
     if (attr_err != hipSuccess) return attr_err;
     const int n_ktiles = (a.N + kBwdBK - 1) / kBwdBK;
     hipLaunchKernelGGL(kern, dim3(n_ktiles * BH), dim3(kBwdThreads), C::BYTES, stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                       static_cast<const T*>(a.dout), a.lse, a.dsum, a.dq_acc, static_cast<T*>(a.dk),
-                       static_cast<T*>(a.dv), a.N, BH, a.scale);
+                       static_cast<const T*>(a.dout), a.lse, a.dsum, static_cast<T*>(a.dk), static_cast<T*>(a.dv),
+                       a.N, BH, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (stages & kStageFinal) {
-    const size_t n4 = rows * D / 4;
-    const dim3 grid((unsigned)((n4 + 255) / 256));
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T>), grid, dim3(256), 0, stream, a.dq_acc, static_cast<T*>(a.dq),
-                       n4, a.scale);
+  if (stages & kStageDq) {
+    constexpr int bytes = 4 * kDqBC * D * (int)sizeof(T);
+    auto kern = fa_bwd_dq_kernel<T, D, CAUSAL>;
+    static const hipError_t attr_err =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (attr_err != hipSuccess) return attr_err;
+    const int n_qtiles = (a.N + kDqBR - 1) / kDqBR;
+    hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(kDqThreads), bytes, stream, static_cast<const T*>(a.q),
+                       static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse,
+                       a.dsum, static_cast<T*>(a.dq), a.N, BH, n_qtiles, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

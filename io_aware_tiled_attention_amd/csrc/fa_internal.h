@@ -31,18 +31,16 @@ struct BwdArgs {
   void* dv;
   int B, H, N, d, causal, dtype;
   float scale;
-  float* dsum;     // [B*H*N]   D_i = do_i . o_i
-  float* dq_acc;   // [B*H*N*d] fp32 dQ accumulator (unscaled)
+  float* dsum;     // [B*H*N]   D_i = do_i . o_i (the workspace)
 };
 
 // Workspace carve-up shared by fa_backward_workspace_size and fa_backward.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline size_t ws_dsum_bytes(size_t rows) { return align256(rows * sizeof(float)); }
-inline size_t ws_dq_bytes(size_t rows, size_t d) { return align256(rows * d * sizeof(float)); }
 
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
-// stage: 1 = preprocess, 2 = accumulate, 4 = finalize (bit mask; 7 = all)
-constexpr int kStagePre = 1, kStageMain = 2, kStageFinal = 4;
+// backward stages (bit mask; 7 = all): D, then dK/dV, then dQ
+constexpr int kStagePre = 1, kStageDkDv = 2, kStageDq = 4;
 hipError_t launch_backward(const BwdArgs& a, int stages, hipStream_t stream);
 
 }  // namespace fa

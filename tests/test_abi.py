@@ -105,7 +105,7 @@ def test_workspace_size_is_linear_in_n_and_aligned():
     for d in (64, 128):
         for n in (1, 17, 4096, 16384):
             rows = 3 * 5 * n
-            want = ((rows * 4 + 255) // 256) * 256 + ((rows * d * 4 + 255) // 256) * 256
+            want = ((rows * 4 + 255) // 256) * 256
             assert fa.workspace_size(3, 5, n, d) == want
     assert fa.workspace_size(1, 1, 0, 64) == 0
     assert fa.workspace_size(1, 1, 16, 48) == 0
@@ -129,12 +129,18 @@ def test_staged_backward_validation():
     assert fa.fa_backward_preprocess(FAKE, FAKE, B, H, N, d, bf, ws, need - 1, None) == 6
     assert fa.fa_backward_preprocess(FAKE, FAKE, B, H, N, 32, bf, ws, need, None) == 3
     assert fa.fa_backward_preprocess(FAKE, FAKE, B, H, 0, d, bf, 0, 0, None) == 0
-    args = [FAKE] * 7
-    assert fa.fa_backward_accumulate(*args, B, H, N, d, 1, 0.1, bf, 0, need, None) == 6
-    bad = list(args)
+    kv_args = [FAKE] * 7          # q, k, v, dout, lse, dk, dv
+    assert fa.fa_backward_dkdv(*kv_args, B, H, N, d, 1, 0.1, bf, 0, need, None) == 6
+    bad = list(kv_args)
     bad[4] = 0  # lse
-    assert fa.fa_backward_accumulate(*bad, B, H, N, d, 1, 0.1, bf, ws, need, None) == 1
-    assert fa.fa_backward_accumulate(*args, B, H, N, d, 1, float("nan"), bf, ws, need, None) == 5
-    assert fa.fa_backward_finalize(0, B, H, N, d, 0.1, bf, ws, need, None) == 1
-    assert fa.fa_backward_finalize(FAKE + 8, B, H, N, d, 0.1, bf, ws, need, None) == 8
-    assert fa.fa_backward_finalize(FAKE, B, H, N, d, 0.1, 3, ws, need, None) == 4
+    assert fa.fa_backward_dkdv(*bad, B, H, N, d, 1, 0.1, bf, ws, need, None) == 1
+    bad = list(kv_args)
+    bad[6] = FAKE + 8  # dv misaligned
+    assert fa.fa_backward_dkdv(*bad, B, H, N, d, 1, 0.1, bf, ws, need, None) == 8
+    assert fa.fa_backward_dkdv(*kv_args, B, H, N, d, 1, float("nan"), bf, ws, need, None) == 5
+    dq_args = [FAKE] * 6          # q, k, v, dout, lse, dq
+    bad = list(dq_args)
+    bad[5] = 0
+    assert fa.fa_backward_dq(*bad, B, H, N, d, 1, 0.1, bf, ws, need, None) == 1
+    assert fa.fa_backward_dq(*dq_args, B, H, N, d, 1, 0.1, 3, ws, need, None) == 4
+    assert fa.fa_backward_dq(*dq_args, -1, H, N, d, 1, 0.1, bf, ws, need, None) == 2
