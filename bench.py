@@ -90,21 +90,22 @@ class Step:
                                      int(self.p.causal), self.p.scale, self.dt, self.stream), "fa_forward")
 
     def bwd_pre(self):
-        self._ck(self.lib.fa_backward_preprocess(self.o.data_ptr(), self.do.data_ptr(), self.p.B, self.p.H,
-                                                 self.p.N, self.p.d, self.dt, self.ws.data_ptr(),
-                                                 self.ws_bytes, self.stream), "fa_backward_preprocess")
+        self._ck(self.lib.fa_backward_preprocess(self.o.data_ptr(), self.do.data_ptr(), self.lse.data_ptr(),
+                                                 self.p.B, self.p.H, self.p.N, self.p.d, self.dt,
+                                                 self.ws.data_ptr(), self.ws_bytes, self.stream),
+                 "fa_backward_preprocess")
 
     def bwd_dkdv(self):
         p = self
         self._ck(self.lib.fa_backward_dkdv(p.q.data_ptr(), p.k.data_ptr(), p.v.data_ptr(), p.do.data_ptr(),
-                                           p.lse.data_ptr(), p.dk.data_ptr(), p.dv.data_ptr(), self.p.B, self.p.H,
+                                           p.dk.data_ptr(), p.dv.data_ptr(), self.p.B, self.p.H,
                                            self.p.N, self.p.d, int(self.p.causal), self.p.scale, self.dt,
                                            p.ws.data_ptr(), self.ws_bytes, self.stream), "fa_backward_dkdv")
 
     def bwd_dq(self):
         p = self
         self._ck(self.lib.fa_backward_dq(p.q.data_ptr(), p.k.data_ptr(), p.v.data_ptr(), p.do.data_ptr(),
-                                         p.lse.data_ptr(), p.dq.data_ptr(), self.p.B, self.p.H, self.p.N, self.p.d,
+                                         p.dq.data_ptr(), self.p.B, self.p.H, self.p.N, self.p.d,
                                          int(self.p.causal), self.p.scale, self.dt, p.ws.data_ptr(), self.ws_bytes,
                                          self.stream), "fa_backward_dq")
 
@@ -158,7 +159,7 @@ def kernel_table(p, avg):
     mm("fwd", "fa_fwd_kernel", fwd_f)
     mm("bwd_dkdv", "fa_bwd_dkdv_kernel", 4 * unit)
     mm("bwd_dq", "fa_bwd_dq_kernel", 3 * unit)
-    pre_bytes = 2 * tens + rows * 4                            # read O, dO; write D
+    pre_bytes = 2 * tens + 3 * rows * 4                        # read O, dO, lse; write D, -lse
     out["bwd_pre"] = {"kernel": "fa_bwd_pre_kernel", "ms": avg["bwd_pre"], "bytes": pre_bytes,
                       "gbs": pre_bytes / avg["bwd_pre"] * 1e-6}
     out["bwd_total"] = {"ms": avg["bwd_pre"] + avg["bwd_dkdv"] + avg["bwd_dq"]}

@@ -82,8 +82,9 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                void* stream);
 
 /*
- * Bytes of device workspace that fa_backward needs: the fp32 row terms
- * D = rowsum(dO o O) ([B,H,N]), 256-byte aligned.  Linear in N: no N x N
+ * Bytes of device workspace that fa_backward needs: two fp32 row statistics
+ * per (batch, head, row) -- D = rowsum(dO o O) and -lse in the kernels'
+ * exponent domain -- each array 256-byte aligned.  Linear in N: no N x N
  * buffer is ever used.  Returns 0 for invalid or empty shapes.
  */
 size_t fa_backward_workspace_size(int B, int H, int N, int d);
@@ -104,27 +105,25 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
 
 /*
  * The three stages that fa_backward enqueues, in order, for callers that
- * schedule or time them separately.  Same arguments, layout and workspace
- * as fa_backward; calling fa_backward_preprocess and then the other two (in
- * either order, both after it) on one stream is exactly fa_backward.
+ * schedule or time them separately.  Same tensors, layout, scale and
+ * workspace as fa_backward; fa_backward_preprocess fills the workspace and
+ * the other two read it, in either order, on the same stream.
  *   fa_backward_preprocess: D_i = do_i . o_i (fp32, the row term of the
  *     softmax Jacobian, "Overview of Flash Attention series", Backward Pass)
- *     into the workspace.
- *   fa_backward_dkdv: recompute S and P from lse key block by key block and
- *     write dK = scale * dS^T Q and dV = P^T dO.
+ *     and -lse_i into the workspace.
+ *   fa_backward_dkdv: recompute S and P key block by key block and write
+ *     dK = scale * dS^T Q and dV = P^T dO.
  *   fa_backward_dq: recompute them query block by query block and write
  *     dQ = scale * dS K.
  */
-int fa_backward_preprocess(const void* o, const void* dout, int B, int H, int N, int d, int dtype,
-                           void* workspace, size_t workspace_bytes, void* stream);
-int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout,
-                     const float* lse, void* dk, void* dv, int B, int H, int N, int d,
-                     int causal, float scale, int dtype, void* workspace,
-                     size_t workspace_bytes, void* stream);
-int fa_backward_dq(const void* q, const void* k, const void* v, const void* dout,
-                   const float* lse, void* dq, int B, int H, int N, int d, int causal,
-                   float scale, int dtype, void* workspace, size_t workspace_bytes,
-                   void* stream);
+int fa_backward_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int N,
+                           int d, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk,
+                     void* dv, int B, int H, int N, int d, int causal, float scale, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+int fa_backward_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                   int B, int H, int N, int d, int causal, float scale, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static English description of an fa_status value (never NULL). */
 const char* fa_strerror(int status);

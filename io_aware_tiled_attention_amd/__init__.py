@@ -129,15 +129,15 @@ def backward_stages(q, k, v, o, do, lse, causal: bool = False, scale: Optional[f
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     dt, s, ws, wn = _dtype_code(q), _stream_ptr(q.device), workspace.data_ptr(), workspace.numel()
-    st = fa_backward_preprocess(o.data_ptr(), do.data_ptr(), B, H, N, d, dt, ws, wn, s)
+    st = fa_backward_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), B, H, N, d, dt, ws, wn, s)
     if st != 0:
         raise FaError(st, "fa_backward_preprocess")
-    st = fa_backward_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                        dq.data_ptr(), B, H, N, d, causal, scale, dt, ws, wn, s)
+    st = fa_backward_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), dq.data_ptr(),
+                        B, H, N, d, causal, scale, dt, ws, wn, s)
     if st != 0:
         raise FaError(st, "fa_backward_dq")
-    st = fa_backward_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                          dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale, dt, ws, wn, s)
+    st = fa_backward_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), dk.data_ptr(),
+                          dv.data_ptr(), B, H, N, d, causal, scale, dt, ws, wn, s)
     if st != 0:
         raise FaError(st, "fa_backward_dkdv")
     return dq, dk, dv

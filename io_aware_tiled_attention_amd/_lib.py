@@ -53,11 +53,11 @@ def load() -> ctypes.CDLL:
         lib.fa_backward.restype = i
         lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
         lib.fa_backward_workspace_size.restype = sz
-        lib.fa_backward_preprocess.argtypes = [vp, vp, i, i, i, i, i, vp, sz, vp]
+        lib.fa_backward_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
         lib.fa_backward_preprocess.restype = i
-        lib.fa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+        lib.fa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
         lib.fa_backward_dkdv.restype = i
-        lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+        lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
         lib.fa_backward_dq.restype = i
         lib.fa_strerror.argtypes = [i]
         lib.fa_strerror.restype = ctypes.c_char_p
@@ -75,19 +75,19 @@ def fa_backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dt
                               float(scale), dtype, workspace, workspace_bytes, stream)
 
 
-def fa_backward_preprocess(o, dout, B, H, N, d, dtype, workspace, workspace_bytes, stream) -> int:
-    return load().fa_backward_preprocess(o, dout, B, H, N, d, dtype, workspace, workspace_bytes, stream)
+def fa_backward_preprocess(o, dout, lse, B, H, N, d, dtype, workspace, workspace_bytes, stream) -> int:
+    return load().fa_backward_preprocess(o, dout, lse, B, H, N, d, dtype, workspace, workspace_bytes, stream)
 
 
-def fa_backward_dkdv(q, k, v, dout, lse, dk, dv, B, H, N, d, causal, scale, dtype,
+def fa_backward_dkdv(q, k, v, dout, dk, dv, B, H, N, d, causal, scale, dtype,
                      workspace, workspace_bytes, stream) -> int:
-    return load().fa_backward_dkdv(q, k, v, dout, lse, dk, dv, B, H, N, d, int(causal),
+    return load().fa_backward_dkdv(q, k, v, dout, dk, dv, B, H, N, d, int(causal),
                                    float(scale), dtype, workspace, workspace_bytes, stream)
 
 
-def fa_backward_dq(q, k, v, dout, lse, dq, B, H, N, d, causal, scale, dtype,
+def fa_backward_dq(q, k, v, dout, dq, B, H, N, d, causal, scale, dtype,
                    workspace, workspace_bytes, stream) -> int:
-    return load().fa_backward_dq(q, k, v, dout, lse, dq, B, H, N, d, int(causal), float(scale),
+    return load().fa_backward_dq(q, k, v, dout, dq, B, H, N, d, int(causal), float(scale),
                                  dtype, workspace, workspace_bytes, stream)
 
 

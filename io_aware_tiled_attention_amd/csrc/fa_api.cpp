@@ -48,9 +48,10 @@ int run_backward(int stages, const void* q, const void* k, const void* v, const 
   if (pre) {
     need[n_need++] = o;
     need[n_need++] = dout;
+    need[n_need++] = lse;
   }
   if (kv || dqs) {
-    const void* ptrs[] = {q, k, v, dout, lse};
+    const void* ptrs[] = {q, k, v, dout};
     for (const void* p : ptrs) need[n_need++] = p;
   }
   if (kv) {
@@ -63,10 +64,11 @@ int run_backward(int stages, const void* q, const void* k, const void* v, const 
   for (int i = 0; i < n_need; ++i)
     if (!aligned16(need[i])) return FA_ERR_ALIGN;
   const size_t rows = (size_t)B * H * N;
-  if (!workspace || workspace_bytes < fa::ws_dsum_bytes(rows)) return FA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < fa::ws_bytes(rows)) return FA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal ? 1 : 0, dtype, scale,
-                static_cast<float*>(workspace)};
+                reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + fa::ws_dsum_bytes(rows))};
   return hip_status(fa::launch_backward(a, stages, static_cast<hipStream_t>(stream)));
 }
 
@@ -89,7 +91,7 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
   bool empty = false;
   if (check_shape(B, H, N, d, FA_BF16, 1.f, &empty) != FA_OK || empty) return 0;
-  return fa::ws_dsum_bytes((size_t)B * H * N);
+  return fa::ws_bytes((size_t)B * H * N);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -99,23 +101,23 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                       d, causal, scale, dtype, workspace, workspace_bytes, stream);
 }
 
-int fa_backward_preprocess(const void* o, const void* dout, int B, int H, int N, int d, int dtype,
+int fa_backward_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int N, int d, int dtype,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  return run_backward(fa::kStagePre, nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr, nullptr, B, H,
-                      N, d, 0, 1.f, dtype, workspace, workspace_bytes, stream);
+  return run_backward(fa::kStagePre, nullptr, nullptr, nullptr, o, dout, lse, nullptr, nullptr, nullptr, B, H, N, d,
+                      0, 1.f, dtype, workspace, workspace_bytes, stream);
 }
 
-int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dk,
-                     void* dv, int B, int H, int N, int d, int causal, float scale, int dtype, void* workspace,
-                     size_t workspace_bytes, void* stream) {
-  return run_backward(fa::kStageDkDv, q, k, v, nullptr, dout, lse, nullptr, dk, dv, B, H, N, d, causal, scale,
+int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv, int B, int H,
+                     int N, int d, int causal, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return run_backward(fa::kStageDkDv, q, k, v, nullptr, dout, nullptr, nullptr, dk, dv, B, H, N, d, causal, scale,
                       dtype, workspace, workspace_bytes, stream);
 }
 
-int fa_backward_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, void* dq,
-                   int B, int H, int N, int d, int causal, float scale, int dtype, void* workspace,
-                   size_t workspace_bytes, void* stream) {
-  return run_backward(fa::kStageDq, q, k, v, nullptr, dout, lse, dq, nullptr, nullptr, B, H, N, d, causal, scale,
+int fa_backward_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, int B, int H, int N,
+                   int d, int causal, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return run_backward(fa::kStageDq, q, k, v, nullptr, dout, nullptr, dq, nullptr, nullptr, B, H, N, d, causal, scale,
                       dtype, workspace, workspace_bytes, stream);
 }
 

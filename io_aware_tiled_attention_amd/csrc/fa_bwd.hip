@@ -13,7 +13,8 @@
 // FlashAttention математически" section 5: recompute instead of store).
 //
 // Three launches on the caller's stream, none of them with atomics:
-//   1. fa_bwd_pre: D_i = rowsum(dO o O) in fp32 into the workspace.
+//   1. fa_bwd_pre: D_i = rowsum(dO o O) in fp32 and -lse_i (in the exponent
+//      domain) into the workspace.
 //   2. fa_bwd_dkdv: a workgroup owns 128 keys (4 waves x 32) and keeps its
 //      slice of K, V and the fp32 accumulators dK^T, dV^T in registers while
 //      sweeping the query blocks that can see them (all blocks, or the blocks
@@ -61,9 +62,13 @@ struct BwdCfg {
 };
 
 // ---------------------------------------------------------------- 1. preprocess
+// Row statistics in the workspace: dsum[i] = D_i = do_i . o_i, and
+// nlse[i] = -lse_i in the exponent domain of T, so that the later kernels
+// form P = ex(s * factor + nlse) with one FMA.
 template <typename T, int D>
 __global__ __launch_bounds__(256)
-void fa_bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __restrict__ dsum, size_t rows) {
+void fa_bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, const float* __restrict__ LSE,
+                       float* __restrict__ dsum, float* __restrict__ nlse, size_t rows) {
   constexpr int VE = 16 / sizeof(T);
   constexpr int CPR = D / VE;                 // threads per row
   constexpr int RPB = 256 / CPR;              // rows per block
@@ -80,14 +85,17 @@ void fa_bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, float*
   }
 #pragma unroll
   for (int off = CPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
-  if (row < rows && tid % CPR == 0) dsum[row] = part;
+  if (row < rows && tid % CPR == 0) {
+    dsum[row] = part;
+    nlse[row] = -ExpDomain<T>::from_lse(LSE[row]);
+  }
 }
 
 // ---------------------------------------------------------------- 2. dK, dV
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1)
+__global__ __launch_bounds__(kBwdThreads, 2)
 void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-                        const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ dsum,
+                        const T* __restrict__ dO, const float* __restrict__ dsum, const float* __restrict__ nlse,
                         T* __restrict__ dK, T* __restrict__ dV, int N, int BH, float scale) {
   using M = Mfma<T>;
   using C = BwdCfg<T, D>;
@@ -102,7 +110,7 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int g = lane >> 5;
   const int r32 = lane & 31;
 
@@ -117,7 +125,7 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
   const rsrc_t rk = make_rsrc(K + head, head_bytes);
   const rsrc_t rv = make_rsrc(V + head, head_bytes);
   const rsrc_t rdo = make_rsrc(dO + head, head_bytes);
-  const rsrc_t rlse = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
+  const rsrc_t rnl = make_rsrc(nlse + (size_t)bh * N, (uint32_t)N * 4u);
   const rsrc_t rdd = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
   const float kfac = X::factor(scale);
 
@@ -140,9 +148,73 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
   auto load_block = [&](int q0b, int st) {
     tile_to_lds<T, D, BQ, kBwdWaves>(rq, C::q(smem, st), q0b, w, lane);
     tile_to_lds<T, D, BQ, kBwdWaves>(rdo, C::dout(smem, st), q0b, w, lane);
-    // lse and D of the block's rows, one float per lane (rows past N read 0)
-    if (w == 0) lds_dma4(rlse, C::lse(smem, st), (q0b + lane) * 4);
+    // -lse and D of the block's rows, one float per lane (rows past N read 0)
+    if (w == 0) lds_dma4(rnl, C::lse(smem, st), (q0b + lane) * 4);
     if (w == 1) lds_dma4(rdd, C::dd(smem, st), (q0b + lane) * 4);
+  };
+
+  // S = Q K^T and dP = dO V^T for 32-row sub-block qs_i: rows = queries,
+  // column = this lane's key.  All A-operand fragments are read from LDS
+  // before the products are issued, so the LDS latency is paid once.
+  auto sdp = [&](const lds_u8* qs, const lds_u8* dos, int qs_i, f32x16& s, f32x16& dp) {
+    Frag aq[D / KC], ado[D / KC];
+#pragma unroll
+    for (int c = 0; c < D / KC; ++c) {
+      const int off = G::off(qs_i * 32 + r32, c * KC + g * KPL);
+      aq[c] = M::lds(qs + off);
+      ado[c] = M::lds(dos + off);
+    }
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int c = 0; c < D / KC; ++c) {
+      s = M::mma(aq[c], kf[c], s);
+      dp = M::mma(ado[c], vf[c], dp);
+    }
+  };
+  // P = ex(S*factor - lse) and dS = P (dP - D) in place; with `lim` >= 0
+  // entries whose row offset acc_row(i, 0) < lim (key > query) get P = 0.
+  auto softmax_grad = [&](const lds_u8* nl_s, const lds_u8* dd_s, int qs_i, f32x16& s, f32x16& dp, bool masked,
+                          int lim) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const f32x4 lz = *(const lds_f32x4*)(nl_s + (qs_i * 32 + 8 * a + 4 * g) * 4);
+      const f32x4 dz = *(const lds_f32x4*)(dd_s + (qs_i * 32 + 8 * a + 4 * g) * 4);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int i = 4 * a + b;
+        float p = X::ex(__builtin_fmaf(s[i], kfac, lz[b]));
+        if (masked) p = (acc_row(i, 0) < lim) ? 0.f : p;
+        s[i] = p;
+        dp[i] = p * (dp[i] - dz[b]);
+      }
+    }
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS (k = the 32 queries of the sub-block);
+  // the transposed fragments of one k-step are read before its products.
+  auto accumulate = [&](const lds_u8* qs, const lds_u8* dos, int qs_i, const f32x16& s, const f32x16& dp) {
+#pragma unroll
+    for (int t = 0; t < 32 / KC; ++t) {
+      Frag a_do[NDB], a_q[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        if constexpr (sizeof(T) == 2) {
+          a_do[db] = lds_tr_frag<D>(dos, qs_i * 32 + 16 * t, db * 32, lane);
+          a_q[db] = lds_tr_frag<D>(qs, qs_i * 32 + 16 * t, db * 32, lane);
+        } else {
+          const int off = G::off(qs_i * 32 + acc_row(t, g), db * 32 + r32);
+          a_do[db] = M::lds(dos + off);
+          a_q[db] = M::lds(qs + off);
+        }
+      }
+      const Frag pb = M::pack(s, t);
+      const Frag dsb = M::pack(dp, t);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dv_acc[db] = M::mma(a_do[db], pb, dv_acc[db]);
+        dk_acc[db] = M::mma(a_q[db], dsb, dk_acc[db]);
+      }
+    }
   };
 
   // Query blocks from the first one that sees these keys to the end.
@@ -160,59 +232,22 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
 
     const lds_u8* qs = C::q(smem, st);
     const lds_u8* dos = C::dout(smem, st);
-    const lds_u8* lse_s = C::lse(smem, st);
+    const lds_u8* nl_s = C::lse(smem, st);
     const lds_u8* dd_s = C::dd(smem, st);
 
+    // every (query, key) pair of the block visible to this wave: no masks
+    const bool full = (!CAUSAL || q0b >= kw0 + kBwdKW - 1) && (kw0 + kBwdKW <= N);
 #pragma unroll
     for (int qs_i = 0; qs_i < QB; ++qs_i) {
       const int qsb = q0b + qs_i * 32;
       // every query of the sub-block precedes every key of the wave: nothing to add
-      if (CAUSAL && qsb + 31 < kw0) continue;
-      // S = Q K^T and dP = dO V^T: rows = queries, column = this lane's key.
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int c = 0; c < D / KC; ++c) {
-        const int off = G::off(qs_i * 32 + r32, c * KC + g * KPL);
-        s = M::mma(M::lds(qs + off), kf[c], s);
-        dp = M::mma(M::lds(dos + off), vf[c], dp);
-      }
-      // P = exp(S - lse), dS = P (dP - D); masked entries (key > query, or a
-      // key past the end) get P = 0.
-      const bool masked = (CAUSAL && qsb < kw0 + kBwdKW - 1) || (kw0 + kBwdKW > N);
+      if (CAUSAL && !full && qsb + 31 < kw0) continue;
+      __builtin_amdgcn_iglp_opt(2);   // interleave the exponentials with the products
+      f32x16 s, dp;
+      sdp(qs, dos, qs_i, s, dp);
       const int lim = (mykey >= N) ? 64 : (CAUSAL ? mykey - (qsb + 4 * g) : -1);
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4 lz = *(const lds_f32x4*)(lse_s + (qs_i * 32 + 8 * a + 4 * g) * 4);
-        const f32x4 dz = *(const lds_f32x4*)(dd_s + (qs_i * 32 + 8 * a + 4 * g) * 4);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int i = 4 * a + b;
-          float p = X::ex(__builtin_fmaf(s[i], kfac, -X::from_lse(lz[b])));
-          if (masked) p = (acc_row(i, 0) < lim) ? 0.f : p;
-          s[i] = p;
-          dp[i] = p * (dp[i] - dz[b]);
-        }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS (k = the 32 queries of the sub-block).
-#pragma unroll
-      for (int t = 0; t < 32 / KC; ++t) {
-        const Frag pb = M::pack(s, t);
-        const Frag dsb = M::pack(dp, t);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          Frag a_do, a_q;
-          if constexpr (sizeof(T) == 2) {
-            a_do = lds_tr_frag<D>(dos, qs_i * 32 + 16 * t, db * 32, lane);
-            a_q = lds_tr_frag<D>(qs, qs_i * 32 + 16 * t, db * 32, lane);
-          } else {
-            const int off = G::off(qs_i * 32 + acc_row(t, g), db * 32 + r32);
-            a_do = M::lds(dos + off);
-            a_q = M::lds(qs + off);
-          }
-          dv_acc[db] = M::mma(a_do, pb, dv_acc[db]);
-          dk_acc[db] = M::mma(a_q, dsb, dk_acc[db]);
-        }
-      }
+      softmax_grad(nl_s, dd_s, qs_i, s, dp, !full, lim);
+      accumulate(qs, dos, qs_i, s, dp);
     }
     wait_vmem();
     __syncthreads();
@@ -242,7 +277,7 @@ constexpr int kDqThreads = kDqWaves * 64;
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kDqThreads, sizeof(T) == 2 ? 2 : 1)
 void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-                      const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ dsum,
+                      const T* __restrict__ dO, const float* __restrict__ dsum, const float* __restrict__ nlse,
                       T* __restrict__ dQ, int N, int BH, int n_qtiles, float scale) {
   using M = Mfma<T>;
   using G = Tile<T, D>;
@@ -257,7 +292,7 @@ void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int g = lane >> 5;
   const int r32 = lane & 31;
 
@@ -284,9 +319,9 @@ void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
     qf[c] = M::load(rq, off);
     dof[c] = M::load(rdo, off);
   }
-  const rsrc_t rlse = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
+  const rsrc_t rnl = make_rsrc(nlse + (size_t)bh * N, (uint32_t)N * 4u);
   const rsrc_t rdd = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
-  const float lse_x = X::from_lse(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rlse, myq * 4, 0, 0)));
+  const float nl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rnl, myq * 4, 0, 0));
   const float dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdd, myq * 4, 0, 0));
 
   const int kv_end = CAUSAL ? min(N, q0 + kDqBR) : N;
@@ -329,17 +364,24 @@ void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
           dp[kb] = M::mma(M::lds(vs + off), dof[c], dp[kb]);
         }
       const bool masked = (CAUSAL && kv0 + kDqBC - 1 > qw0) || (kv0 + kDqBC > N);
-      const int last = CAUSAL ? min(N - 1, myq) : N - 1;
+      if (masked) {
+        // keys allowed for this lane: key <= min(N-1, myq) (causal) or key <= N-1
+        const int last = CAUSAL ? min(N - 1, myq) : N - 1;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int lim = last - (kv0 + kb * 32 + 4 * g);
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int lim = last - (kv0 + kb * 32 + 4 * g);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = X::ex(__builtin_fmaf(s[kb][i], kfac, -lse_x));
-          if (masked) p = (acc_row(i, 0) > lim) ? 0.f : p;
-          dp[kb][i] = p * (dp[kb][i] - dd);
+          for (int i = 0; i < 16; ++i) s[kb][i] = (acc_row(i, 0) > lim) ? kNegInf : s[kb][i];
         }
       }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          // masked scores are -inf and kfac > 0, so P = 0 there
+          const float p = X::ex(__builtin_fmaf(s[kb][i], kfac, nl));
+          dp[kb][i] = p * (dp[kb][i] - dd);
+        }
       // dQ^T += K^T dS^T, dS^T straight from registers (B operand), K^T from
       // the K tile through the transpose read (A operand).
 #pragma unroll
@@ -378,7 +420,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     constexpr int RPB = 256 / (D / (16 / (int)sizeof(T)));
     const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
     hipLaunchKernelGGL((fa_bwd_pre_kernel<T, D>), grid, dim3(256), 0, stream, static_cast<const T*>(a.o),
-                       static_cast<const T*>(a.dout), a.dsum, rows);
+                       static_cast<const T*>(a.dout), a.lse, a.dsum, a.nlse, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -391,8 +433,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     const int n_ktiles = (a.N + kBwdBK - 1) / kBwdBK;
     hipLaunchKernelGGL(kern, dim3(n_ktiles * BH), dim3(kBwdThreads), C::BYTES, stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                       static_cast<const T*>(a.dout), a.lse, a.dsum, static_cast<T*>(a.dk), static_cast<T*>(a.dv),
-                       a.N, BH, a.scale);
+                       static_cast<const T*>(a.dout), a.dsum, a.nlse, static_cast<T*>(a.dk),
+                       static_cast<T*>(a.dv), a.N, BH, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -404,8 +446,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     if (attr_err != hipSuccess) return attr_err;
     const int n_qtiles = (a.N + kDqBR - 1) / kDqBR;
     hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(kDqThreads), bytes, stream, static_cast<const T*>(a.q),
-                       static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<const T*>(a.dout), a.lse,
-                       a.dsum, static_cast<T*>(a.dq), a.N, BH, n_qtiles, a.scale);
+                       static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<const T*>(a.dout),
+                       a.dsum, a.nlse, static_cast<T*>(a.dq), a.N, BH, n_qtiles, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

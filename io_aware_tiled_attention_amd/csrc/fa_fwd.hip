@@ -74,7 +74,7 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int g = lane >> 5;
   const int r32 = lane & 31;
 

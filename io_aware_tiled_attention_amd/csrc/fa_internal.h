@@ -31,12 +31,14 @@ struct BwdArgs {
   void* dv;
   int B, H, N, d, causal, dtype;
   float scale;
-  float* dsum;     // [B*H*N]   D_i = do_i . o_i (the workspace)
+  float* dsum;     // [B*H*N]   D_i = do_i . o_i          (workspace)
+  float* nlse;     // [B*H*N]   -lse_i, exponent domain   (workspace)
 };
 
 // Workspace carve-up shared by fa_backward_workspace_size and fa_backward.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline size_t ws_dsum_bytes(size_t rows) { return align256(rows * sizeof(float)); }
+inline size_t ws_bytes(size_t rows) { return 2 * ws_dsum_bytes(rows); }
 
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
 // backward stages (bit mask; 7 = all): D, then dK/dV, then dQ

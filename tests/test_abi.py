@@ -105,7 +105,7 @@ def test_workspace_size_is_linear_in_n_and_aligned():
     for d in (64, 128):
         for n in (1, 17, 4096, 16384):
             rows = 3 * 5 * n
-            want = ((rows * 4 + 255) // 256) * 256
+            want = 2 * (((rows * 4 + 255) // 256) * 256)
             assert fa.workspace_size(3, 5, n, d) == want
     assert fa.workspace_size(1, 1, 0, 64) == 0
     assert fa.workspace_size(1, 1, 16, 48) == 0
@@ -125,22 +125,23 @@ def test_staged_backward_validation():
     B, H, N, d = 1, 2, 64, 64
     ws, need = 0x100000, fa.workspace_size(1, 2, 64, 64)
     bf = _lib.FA_BF16
-    assert fa.fa_backward_preprocess(0, FAKE, B, H, N, d, bf, ws, need, None) == 1
-    assert fa.fa_backward_preprocess(FAKE, FAKE, B, H, N, d, bf, ws, need - 1, None) == 6
-    assert fa.fa_backward_preprocess(FAKE, FAKE, B, H, N, 32, bf, ws, need, None) == 3
-    assert fa.fa_backward_preprocess(FAKE, FAKE, B, H, 0, d, bf, 0, 0, None) == 0
-    kv_args = [FAKE] * 7          # q, k, v, dout, lse, dk, dv
+    assert fa.fa_backward_preprocess(0, FAKE, FAKE, B, H, N, d, bf, ws, need, None) == 1
+    assert fa.fa_backward_preprocess(FAKE, FAKE, 0, B, H, N, d, bf, ws, need, None) == 1
+    assert fa.fa_backward_preprocess(FAKE, FAKE, FAKE, B, H, N, d, bf, ws, need - 1, None) == 6
+    assert fa.fa_backward_preprocess(FAKE, FAKE, FAKE, B, H, N, 32, bf, ws, need, None) == 3
+    assert fa.fa_backward_preprocess(FAKE, FAKE, FAKE, B, H, 0, d, bf, 0, 0, None) == 0
+    kv_args = [FAKE] * 6          # q, k, v, dout, dk, dv
     assert fa.fa_backward_dkdv(*kv_args, B, H, N, d, 1, 0.1, bf, 0, need, None) == 6
     bad = list(kv_args)
-    bad[4] = 0  # lse
+    bad[3] = 0  # dout
     assert fa.fa_backward_dkdv(*bad, B, H, N, d, 1, 0.1, bf, ws, need, None) == 1
     bad = list(kv_args)
-    bad[6] = FAKE + 8  # dv misaligned
+    bad[5] = FAKE + 8  # dv misaligned
     assert fa.fa_backward_dkdv(*bad, B, H, N, d, 1, 0.1, bf, ws, need, None) == 8
     assert fa.fa_backward_dkdv(*kv_args, B, H, N, d, 1, float("nan"), bf, ws, need, None) == 5
-    dq_args = [FAKE] * 6          # q, k, v, dout, lse, dq
+    dq_args = [FAKE] * 5          # q, k, v, dout, dq
     bad = list(dq_args)
-    bad[5] = 0
+    bad[4] = 0
     assert fa.fa_backward_dq(*bad, B, H, N, d, 1, 0.1, bf, ws, need, None) == 1
     assert fa.fa_backward_dq(*dq_args, B, H, N, d, 1, 0.1, 3, ws, need, None) == 4
     assert fa.fa_backward_dq(*dq_args, -1, H, N, d, 1, 0.1, bf, ws, need, None) == 2
