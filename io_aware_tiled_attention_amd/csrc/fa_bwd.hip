@@ -267,6 +267,197 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
     }
 }
 
+// ---------------------------------------------------------------- 2b. dK, dV (bf16)
+// Eight waves over 128 keys: waves w and w + 4 own the same 32 keys (slice
+// w % 4) and take the first and the second 32-row query sub-block of every
+// 64-row block, so each SIMD runs two waves.  K and V stay resident in LDS
+// (their B-operand fragments are read per product instead of held in
+// registers), which is what makes two waves fit.  At the end the two waves of
+// a slice exchange partial sums through LDS: the first group finishes dK,
+// the second dV.
+constexpr int kKvWaves = 8;
+constexpr int kKvThreads = kKvWaves * 64;
+
+template <int D>
+struct KvCfg {
+  using G = Tile<bf16, D>;
+  static constexpr int BQ = 64;                         // query rows per block (2 sub-blocks)
+  static constexpr int KTILE = kBwdBK * G::R;           // K (or V) rows of the workgroup
+  static constexpr int QTILE = BQ * G::R;
+  static constexpr int STAGE = 2 * QTILE + 2 * 64 * 4;  // Q, dO, -lse, D
+  static constexpr int BYTES = 2 * KTILE + 2 * STAGE;
+  static constexpr int NACC = D / 32 * 16;              // accumulator registers per lane (dK or dV)
+  static_assert(4 * NACC * 64 * 4 <= 2 * KTILE && 4 * NACC * 64 * 4 <= 2 * STAGE, "exchange fits");
+  __device__ static lds_u8* k(lds_u8* b) { return b; }
+  __device__ static lds_u8* v(lds_u8* b) { return b + KTILE; }
+  __device__ static lds_u8* q(lds_u8* b, int st) { return b + 2 * KTILE + st * STAGE; }
+  __device__ static lds_u8* dout(lds_u8* b, int st) { return q(b, st) + QTILE; }
+  __device__ static lds_u8* nl(lds_u8* b, int st) { return q(b, st) + 2 * QTILE; }
+  __device__ static lds_u8* dd(lds_u8* b, int st) { return q(b, st) + 2 * QTILE + 256; }
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kKvThreads, 1)
+void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                             const bf16* __restrict__ dO, const float* __restrict__ dsum,
+                             const float* __restrict__ nlse, bf16* __restrict__ dK, bf16* __restrict__ dV, int N,
+                             int BH, float scale) {
+  using M = Mfma<bf16>;
+  using C = KvCfg<D>;
+  using G = Tile<bf16, D>;
+  using X = ExpDomain<bf16>;
+  using Frag = M::Frag;
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  constexpr int KPL = M::KPL, KC = M::KC;
+  constexpr int NDB = D / 32, BQ = C::BQ;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
+  lds_u8* smem = (lds_u8*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int slice = w & 3;                                   // 32-key slice
+  const int grp = w >> 2;                                    // query sub-block of each block
+  const int g = lane >> 5;
+  const int r32 = lane & 31;
+
+  const int bh = blockIdx.x % BH;
+  const int kt = blockIdx.x / BH;             // causal: low key tiles (most work) first
+  const int k0 = kt * kBwdBK;
+  const int kw0 = k0 + slice * kBwdKW;
+  const int mykey = kw0 + r32;
+  const size_t head = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * G::R;
+  const rsrc_t rq = make_rsrc(Q + head, head_bytes);
+  const rsrc_t rk = make_rsrc(K + head, head_bytes);
+  const rsrc_t rv = make_rsrc(V + head, head_bytes);
+  const rsrc_t rdo = make_rsrc(dO + head, head_bytes);
+  const rsrc_t rnl = make_rsrc(nlse + (size_t)bh * N, (uint32_t)N * 4u);
+  const rsrc_t rdd = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
+  const float kfac = X::factor(scale);
+
+  f32x16 dv_acc[NDB], dk_acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dv_acc[db] = f32x16{};
+    dk_acc[db] = f32x16{};
+  }
+
+  auto load_block = [&](int q0b, int st) {
+    tile_to_lds<bf16, D, BQ, kKvWaves>(rq, C::q(smem, st), q0b, w, lane);
+    tile_to_lds<bf16, D, BQ, kKvWaves>(rdo, C::dout(smem, st), q0b, w, lane);
+    if (w == 0) lds_dma4(rnl, C::nl(smem, st), (q0b + lane) * 4);
+    if (w == 1) lds_dma4(rdd, C::dd(smem, st), (q0b + lane) * 4);
+  };
+
+  const int q_begin = CAUSAL ? k0 : 0;
+  const int nblocks = (N - q_begin + BQ - 1) / BQ;
+
+  tile_to_lds<bf16, D, kBwdBK, kKvWaves>(rk, C::k(smem), k0, w, lane);
+  tile_to_lds<bf16, D, kBwdBK, kKvWaves>(rv, C::v(smem), k0, w, lane);
+  load_block(q_begin, 0);
+  wait_vmem();
+  __syncthreads();
+
+  const lds_u8* ks = C::k(smem);
+  const lds_u8* vs = C::v(smem);
+
+  for (int it = 0; it < nblocks; ++it) {
+    const int q0b = q_begin + it * BQ;
+    const int st = it & 1;
+    if (it + 1 < nblocks) load_block(q0b + BQ, st ^ 1);
+
+    const int qsb = q0b + grp * 32;                        // this wave's 32 query rows
+    // skip: every query of the sub-block precedes every key of the slice
+    if (!(CAUSAL && qsb + 31 < kw0)) {
+      const lds_u8* qs = C::q(smem, st);
+      const lds_u8* dos = C::dout(smem, st);
+      const lds_u8* nl_s = C::nl(smem, st);
+      const lds_u8* dd_s = C::dd(smem, st);
+      const int row0 = grp * 32;
+      __builtin_amdgcn_iglp_opt(2);   // interleave the exponentials with the products
+
+      // S = Q K^T and dP = dO V^T: rows = queries, column = this lane's key.
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int c = 0; c < D / KC; ++c) {
+        const int offq = G::off(row0 + r32, c * KC + g * KPL);
+        const int offk = G::off(slice * 32 + r32, c * KC + g * KPL);
+        s = M::mma(M::lds(qs + offq), M::lds(ks + offk), s);
+        dp = M::mma(M::lds(dos + offq), M::lds(vs + offk), dp);
+      }
+      // P = ex(S*factor - lse), dS = P (dP - D); masked (key > query, or a key
+      // past the end) -> P = 0.
+      const bool masked = (CAUSAL && qsb < kw0 + kBwdKW - 1) || (kw0 + kBwdKW > N);
+      const int lim = (mykey >= N) ? 64 : (CAUSAL ? mykey - (qsb + 4 * g) : -1);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 lz = *(const lds_f32x4*)(nl_s + (row0 + 8 * a + 4 * g) * 4);
+        const f32x4 dz = *(const lds_f32x4*)(dd_s + (row0 + 8 * a + 4 * g) * 4);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int i = 4 * a + b;
+          float p = X::ex(__builtin_fmaf(s[i], kfac, lz[b]));
+          if (masked) p = (acc_row(i, 0) < lim) ? 0.f : p;
+          s[i] = p;
+          dp[i] = p * (dp[i] - dz[b]);
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows.
+#pragma unroll
+      for (int t = 0; t < 32 / KC; ++t) {
+        const Frag pb = M::pack(s, t);
+        const Frag dsb = M::pack(dp, t);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dv_acc[db] = M::mma(lds_tr_frag<D>(dos, row0 + 16 * t, db * 32, lane), pb, dv_acc[db]);
+          dk_acc[db] = M::mma(lds_tr_frag<D>(qs, row0 + 16 * t, db * 32, lane), dsb, dk_acc[db]);
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // Combine the two query halves of each slice: group 1 hands its dK partial to
+  // group 0 (through the K/V area), group 0 hands its dV partial to group 1
+  // (through the staging area); partials are laid out [slice][reg/4][lane][4].
+  lds_u8* xk = C::k(smem) + slice * (C::NACC * 64 * 4);
+  lds_u8* xv = C::q(smem, 0) + slice * (C::NACC * 64 * 4);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int off = ((db * 4 + a) * 64 + lane) * 16;
+      if (grp == 1) {
+        const f32x4 x = {dk_acc[db][4 * a], dk_acc[db][4 * a + 1], dk_acc[db][4 * a + 2], dk_acc[db][4 * a + 3]};
+        *(__attribute__((address_space(3))) f32x4*)(xk + off) = x;
+      } else {
+        const f32x4 x = {dv_acc[db][4 * a], dv_acc[db][4 * a + 1], dv_acc[db][4 * a + 2], dv_acc[db][4 * a + 3]};
+        *(__attribute__((address_space(3))) f32x4*)(xv + off) = x;
+      }
+    }
+  __syncthreads();
+  const rsrc_t rdk = make_rsrc(dK + head, head_bytes);
+  const rsrc_t rdv = make_rsrc(dV + head, head_bytes);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int xo = ((db * 4 + a) * 64 + lane) * 16;
+      const int off = mykey * G::R + (db * 32 + 8 * a + 4 * g) * 2;
+      if (grp == 0) {
+        const f32x4 o = *(const __attribute__((address_space(3))) f32x4*)(xk + xo);
+        store4<bf16>(rdk, off, (dk_acc[db][4 * a] + o[0]) * scale, (dk_acc[db][4 * a + 1] + o[1]) * scale,
+                     (dk_acc[db][4 * a + 2] + o[2]) * scale, (dk_acc[db][4 * a + 3] + o[3]) * scale);
+      } else {
+        const f32x4 o = *(const __attribute__((address_space(3))) f32x4*)(xv + xo);
+        store4<bf16>(rdv, off, dv_acc[db][4 * a] + o[0], dv_acc[db][4 * a + 1] + o[1], dv_acc[db][4 * a + 2] + o[2],
+                     dv_acc[db][4 * a + 3] + o[3]);
+      }
+    }
+}
+
 // ---------------------------------------------------------------- 3. dQ
 constexpr int kDqWaves = 4;
 constexpr int kDqQW = 32;                       // query rows per wave
@@ -424,7 +615,20 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (stages & kStageDkDv) {
+  if ((stages & kStageDkDv) && sizeof(T) == 2) {
+    using C = KvCfg<D>;
+    auto kern = fa_bwd_dkdv_bf16_kernel<D, CAUSAL>;
+    static const hipError_t attr_err =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::BYTES);
+    if (attr_err != hipSuccess) return attr_err;
+    const int n_ktiles = (a.N + kBwdBK - 1) / kBwdBK;
+    hipLaunchKernelGGL(kern, dim3(n_ktiles * BH), dim3(kKvThreads), C::BYTES, stream,
+                       static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
+                       static_cast<const bf16*>(a.dout), a.dsum, a.nlse, static_cast<bf16*>(a.dk),
+                       static_cast<bf16*>(a.dv), a.N, BH, a.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (stages & kStageDkDv) {
     using C = BwdCfg<T, D>;
     auto kern = fa_bwd_dkdv_kernel<T, D, CAUSAL>;
     static const hipError_t attr_err =
