@@ -272,9 +272,12 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
 // w % 4) and take the first and the second 32-row query sub-block of every
 // 64-row block, so each SIMD runs two waves.  K and V stay resident in LDS
 // (their B-operand fragments are read per product instead of held in
-// registers), which is what makes two waves fit.  At the end the two waves of
-// a slice exchange partial sums through LDS: the first group finishes dK,
-// the second dV.
+// registers), which is what makes two waves fit.  Every LDS address is a
+// per-lane offset computed once plus a compile-time constant: the block loop
+// is unrolled over the two staging buffers, and blocks that cross no diagonal
+// and no end of the sequence run a body without any masking.  At the end the
+// two waves of a slice exchange partial sums through LDS: the first group
+// finishes dK, the second dV.
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = kKvWaves * 64;
 
@@ -284,16 +287,19 @@ struct KvCfg {
   static constexpr int BQ = 64;                         // query rows per block (2 sub-blocks)
   static constexpr int KTILE = kBwdBK * G::R;           // K (or V) rows of the workgroup
   static constexpr int QTILE = BQ * G::R;
-  static constexpr int STAGE = 2 * QTILE + 2 * 64 * 4;  // Q, dO, -lse, D
-  static constexpr int BYTES = 2 * KTILE + 2 * STAGE;
+  static constexpr int STAGE = 1024 + 2 * QTILE;       // -lse, D (1 KiB slot), Q, dO
+  // [stage 0][stage 1][K][V]: stage-relative addresses fit the 16-bit
+  // immediate offset of ds_read; K and V get a base register of their own.
+  static constexpr int NL0 = 0;
+  static constexpr int DD0 = 256;
+  static constexpr int Q0 = 1024;
+  static constexpr int DO0 = 1024 + QTILE;
+  static constexpr int KOFF = 2 * STAGE;
+  static constexpr int VOFF = KOFF + KTILE;
+  static constexpr int BYTES = 2 * STAGE + 2 * KTILE;
   static constexpr int NACC = D / 32 * 16;              // accumulator registers per lane (dK or dV)
   static_assert(4 * NACC * 64 * 4 <= 2 * KTILE && 4 * NACC * 64 * 4 <= 2 * STAGE, "exchange fits");
-  __device__ static lds_u8* k(lds_u8* b) { return b; }
-  __device__ static lds_u8* v(lds_u8* b) { return b + KTILE; }
-  __device__ static lds_u8* q(lds_u8* b, int st) { return b + 2 * KTILE + st * STAGE; }
-  __device__ static lds_u8* dout(lds_u8* b, int st) { return q(b, st) + QTILE; }
-  __device__ static lds_u8* nl(lds_u8* b, int st) { return q(b, st) + 2 * QTILE; }
-  __device__ static lds_u8* dd(lds_u8* b, int st) { return q(b, st) + 2 * QTILE + 256; }
+  static_assert(STAGE + DO0 + 16 * G::R < 65536, "stage offsets fit the ds_read immediate");
 };
 
 template <int D, bool CAUSAL>
@@ -308,9 +314,11 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
   using X = ExpDomain<bf16>;
   using Frag = M::Frag;
   typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   constexpr int KPL = M::KPL, KC = M::KC;
-  constexpr int NDB = D / 32, BQ = C::BQ;
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
+  constexpr int NDB = D / 32, NC = D / KC, BQ = C::BQ;
+  // static, so that every LDS address is known at compile time
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[C::BYTES];
   lds_u8* smem = (lds_u8*)smem_raw;
 
   const int tid = threadIdx.x;
@@ -336,6 +344,28 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
   const rsrc_t rdd = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
   const float kfac = X::factor(scale);
 
+  // Loop-invariant per-lane LDS offsets.  The swizzle depends on the row
+  // modulo 16 only, so an offset computed for rows 0..31 holds for every
+  // 16-row-aligned shift of them.
+  //   qa[c]: A fragment (row r32 of this wave's query sub-block, k-chunk c)
+  //   ka[c]: B fragment (row r32 of this wave's key slice) in the K tile
+  //   tq[db][e]: transposed fragment reads (rows 4g + (j>>2) + 8e, columns
+  //              db*32 + 16h + 4(j&3)) of this wave's query sub-block
+  int qa[NC], ka[NC], tq[NDB][2];
+  {
+    const int j = lane & 15, h = (lane >> 4) & 1;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qa[c] = G::off(grp * 32 + r32, c * KC + g * KPL);
+      ka[c] = C::KOFF + G::off(slice * 32 + r32, c * KC + g * KPL);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) tq[db][e] = G::off(grp * 32 + 4 * g + (j >> 2) + 8 * e, db * 32 + 16 * h + 4 * (j & 3));
+  }
+  const int stat_off = (grp * 32 + 4 * g) * 4;
+
   f32x16 dv_acc[NDB], dk_acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
@@ -344,86 +374,133 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
   }
 
   auto load_block = [&](int q0b, int st) {
-    tile_to_lds<bf16, D, BQ, kKvWaves>(rq, C::q(smem, st), q0b, w, lane);
-    tile_to_lds<bf16, D, BQ, kKvWaves>(rdo, C::dout(smem, st), q0b, w, lane);
-    if (w == 0) lds_dma4(rnl, C::nl(smem, st), (q0b + lane) * 4);
-    if (w == 1) lds_dma4(rdd, C::dd(smem, st), (q0b + lane) * 4);
+    lds_u8* sb = smem + st * C::STAGE;
+    tile_to_lds<bf16, D, BQ, kKvWaves>(rq, sb + C::Q0, q0b, w, lane);
+    tile_to_lds<bf16, D, BQ, kKvWaves>(rdo, sb + C::DO0, q0b, w, lane);
+    if (w == 0) lds_dma4(rnl, sb + C::NL0, (q0b + lane) * 4);
+    if (w == 1) lds_dma4(rdd, sb + C::DD0, (q0b + lane) * 4);
   };
 
   const int q_begin = CAUSAL ? k0 : 0;
   const int nblocks = (N - q_begin + BQ - 1) / BQ;
 
-  tile_to_lds<bf16, D, kBwdBK, kKvWaves>(rk, C::k(smem), k0, w, lane);
-  tile_to_lds<bf16, D, kBwdBK, kKvWaves>(rv, C::v(smem), k0, w, lane);
+  tile_to_lds<bf16, D, kBwdBK, kKvWaves>(rk, smem + C::KOFF, k0, w, lane);
+  tile_to_lds<bf16, D, kBwdBK, kKvWaves>(rv, smem + C::VOFF, k0, w, lane);
   load_block(q_begin, 0);
   wait_vmem();
   __syncthreads();
 
-  const lds_u8* ks = C::k(smem);
-  const lds_u8* vs = C::v(smem);
-
-  for (int it = 0; it < nblocks; ++it) {
+  // One 64-row query block from staging buffer ST; MASKED also handles the
+  // causal diagonal and keys past the end of the sequence.
+  auto block = [&](int it, auto st_c, auto masked_c) {
+    constexpr int ST = decltype(st_c)::value;
+    constexpr bool MASKED = decltype(masked_c)::value;
     const int q0b = q_begin + it * BQ;
-    const int st = it & 1;
-    if (it + 1 < nblocks) load_block(q0b + BQ, st ^ 1);
-
-    const int qsb = q0b + grp * 32;                        // this wave's 32 query rows
-    // skip: every query of the sub-block precedes every key of the slice
-    if (!(CAUSAL && qsb + 31 < kw0)) {
-      const lds_u8* qs = C::q(smem, st);
-      const lds_u8* dos = C::dout(smem, st);
-      const lds_u8* nl_s = C::nl(smem, st);
-      const lds_u8* dd_s = C::dd(smem, st);
-      const int row0 = grp * 32;
-      __builtin_amdgcn_iglp_opt(2);   // interleave the exponentials with the products
-
+    if (it + 1 < nblocks) load_block(q0b + BQ, ST ^ 1);
+    const int qsb = q0b + grp * 32;   // this wave's 32 query rows
+    bool run = true, diag = false;
+    if constexpr (MASKED) {
+      run = !(CAUSAL && qsb + 31 < kw0);   // some query reaches some key of the slice
+      diag = (CAUSAL && qsb < kw0 + kBwdKW - 1) || (kw0 + kBwdKW > N);
+    }
+    if (run) {
+      const lds_u8* sb = smem + ST * C::STAGE;
       // S = Q K^T and dP = dO V^T: rows = queries, column = this lane's key.
       f32x16 s = f32x16{}, dp = f32x16{};
+      Frag fq[2], fd[2], fk[2], fv[2];
+      fq[0] = M::lds(sb + C::Q0 + qa[0]);
+      fd[0] = M::lds(sb + C::DO0 + qa[0]);
+      fk[0] = M::lds(smem + ka[0]);
+      fv[0] = M::lds(smem + ka[0] + C::KTILE);
 #pragma unroll
-      for (int c = 0; c < D / KC; ++c) {
-        const int offq = G::off(row0 + r32, c * KC + g * KPL);
-        const int offk = G::off(slice * 32 + r32, c * KC + g * KPL);
-        s = M::mma(M::lds(qs + offq), M::lds(ks + offk), s);
-        dp = M::mma(M::lds(dos + offq), M::lds(vs + offk), dp);
+      for (int c = 0; c < NC; ++c) {
+        const int cur = c & 1;
+        if (c + 1 < NC) {
+          fq[cur ^ 1] = M::lds(sb + C::Q0 + qa[c + 1]);
+          fd[cur ^ 1] = M::lds(sb + C::DO0 + qa[c + 1]);
+          fk[cur ^ 1] = M::lds(smem + ka[c + 1]);
+          fv[cur ^ 1] = M::lds(smem + ka[c + 1] + C::KTILE);
+        }
+        s = M::mma(fq[cur], fk[cur], s);
+        dp = M::mma(fd[cur], fv[cur], dp);
+        __builtin_amdgcn_sched_barrier(0);   // keep the reads one step ahead
       }
       // P = ex(S*factor - lse), dS = P (dP - D); masked (key > query, or a key
       // past the end) -> P = 0.
-      const bool masked = (CAUSAL && qsb < kw0 + kBwdKW - 1) || (kw0 + kBwdKW > N);
       const int lim = (mykey >= N) ? 64 : (CAUSAL ? mykey - (qsb + 4 * g) : -1);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const f32x4 lz = *(const lds_f32x4*)(nl_s + (row0 + 8 * a + 4 * g) * 4);
-        const f32x4 dz = *(const lds_f32x4*)(dd_s + (row0 + 8 * a + 4 * g) * 4);
+        const f32x4 lz = *(const lds_f32x4*)(sb + C::NL0 + stat_off + 32 * a);
+        const f32x4 dz = *(const lds_f32x4*)(sb + C::DD0 + stat_off + 32 * a);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int i = 4 * a + b;
           float p = X::ex(__builtin_fmaf(s[i], kfac, lz[b]));
-          if (masked) p = (acc_row(i, 0) < lim) ? 0.f : p;
+          if constexpr (MASKED) {
+            if (diag) p = (acc_row(i, 0) < lim) ? 0.f : p;
+          }
           s[i] = p;
           dp[i] = p * (dp[i] - dz[b]);
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows.
+      auto tr = [&](int base, int t, int db) {
+        union { s16x4 h[2]; Frag f; } u;
+        u.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + base + tq[db][0] + t * 16 * G::R));
+        u.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + base + tq[db][1] + t * 16 * G::R));
+        return u.f;
+      };
 #pragma unroll
       for (int t = 0; t < 32 / KC; ++t) {
         const Frag pb = M::pack(s, t);
         const Frag dsb = M::pack(dp, t);
+        Frag td[2], tqf[2];
+        td[0] = tr(C::DO0, t, 0);
+        tqf[0] = tr(C::Q0, t, 0);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          dv_acc[db] = M::mma(lds_tr_frag<D>(dos, row0 + 16 * t, db * 32, lane), pb, dv_acc[db]);
-          dk_acc[db] = M::mma(lds_tr_frag<D>(qs, row0 + 16 * t, db * 32, lane), dsb, dk_acc[db]);
+          const int cur = db & 1;
+          if (db + 1 < NDB) {
+            td[cur ^ 1] = tr(C::DO0, t, db + 1);
+            tqf[cur ^ 1] = tr(C::Q0, t, db + 1);
+          }
+          dv_acc[db] = M::mma(td[cur], pb, dv_acc[db]);
+          dk_acc[db] = M::mma(tqf[cur], dsb, dk_acc[db]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
     wait_vmem();
     __syncthreads();
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using Msk = std::integral_constant<bool, true>;
+  using NoMsk = std::integral_constant<bool, false>;
+  // Blocks 0 and 1 hold the causal diagonal of the 128 keys; a key tile that
+  // reaches past the end of the sequence is masked throughout.
+  const bool ktail = k0 + kBwdBK > N;
+  const int n_masked = ktail ? nblocks : (CAUSAL ? min(2, nblocks) : 0);
+  int it = 0;
+  for (; it < n_masked; it += 2) {
+    block(it, S0{}, Msk{});
+    if (it + 1 >= n_masked) { ++it; break; }
+    block(it + 1, S1{}, Msk{});
+  }
+  // n_masked is even unless it covers every block, so the unmasked blocks
+  // start on staging buffer 0.
+  for (; it < nblocks; it += 2) {
+    block(it, S0{}, NoMsk{});
+    if (it + 1 >= nblocks) break;
+    block(it + 1, S1{}, NoMsk{});
   }
 
   // Combine the two query halves of each slice: group 1 hands its dK partial to
   // group 0 (through the K/V area), group 0 hands its dV partial to group 1
   // (through the staging area); partials are laid out [slice][reg/4][lane][4].
-  lds_u8* xk = C::k(smem) + slice * (C::NACC * 64 * 4);
-  lds_u8* xv = C::q(smem, 0) + slice * (C::NACC * 64 * 4);
+  lds_u8* xk = smem + C::KOFF + slice * (C::NACC * 64 * 4);
+  lds_u8* xv = smem + slice * (C::NACC * 64 * 4);
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -431,10 +508,10 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
       const int off = ((db * 4 + a) * 64 + lane) * 16;
       if (grp == 1) {
         const f32x4 x = {dk_acc[db][4 * a], dk_acc[db][4 * a + 1], dk_acc[db][4 * a + 2], dk_acc[db][4 * a + 3]};
-        *(__attribute__((address_space(3))) f32x4*)(xk + off) = x;
+        *(lds_f32x4*)(xk + off) = x;
       } else {
         const f32x4 x = {dv_acc[db][4 * a], dv_acc[db][4 * a + 1], dv_acc[db][4 * a + 2], dv_acc[db][4 * a + 3]};
-        *(__attribute__((address_space(3))) f32x4*)(xv + off) = x;
+        *(lds_f32x4*)(xv + off) = x;
       }
     }
   __syncthreads();
@@ -447,11 +524,11 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
       const int xo = ((db * 4 + a) * 64 + lane) * 16;
       const int off = mykey * G::R + (db * 32 + 8 * a + 4 * g) * 2;
       if (grp == 0) {
-        const f32x4 o = *(const __attribute__((address_space(3))) f32x4*)(xk + xo);
+        const f32x4 o = *(const lds_f32x4*)(xk + xo);
         store4<bf16>(rdk, off, (dk_acc[db][4 * a] + o[0]) * scale, (dk_acc[db][4 * a + 1] + o[1]) * scale,
                      (dk_acc[db][4 * a + 2] + o[2]) * scale, (dk_acc[db][4 * a + 3] + o[3]) * scale);
       } else {
-        const f32x4 o = *(const __attribute__((address_space(3))) f32x4*)(xv + xo);
+        const f32x4 o = *(const lds_f32x4*)(xv + xo);
         store4<bf16>(rdv, off, dv_acc[db][4 * a] + o[0], dv_acc[db][4 * a + 1] + o[1], dv_acc[db][4 * a + 2] + o[2],
                      dv_acc[db][4 * a + 3] + o[3]);
       }
@@ -616,13 +693,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if ((stages & kStageDkDv) && sizeof(T) == 2) {
-    using C = KvCfg<D>;
     auto kern = fa_bwd_dkdv_bf16_kernel<D, CAUSAL>;
-    static const hipError_t attr_err =
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::BYTES);
-    if (attr_err != hipSuccess) return attr_err;
     const int n_ktiles = (a.N + kBwdBK - 1) / kBwdBK;
-    hipLaunchKernelGGL(kern, dim3(n_ktiles * BH), dim3(kKvThreads), C::BYTES, stream,
+    hipLaunchKernelGGL(kern, dim3(n_ktiles * BH), dim3(kKvThreads), 0, stream,
                        static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
                        static_cast<const bf16*>(a.dout), a.dsum, a.nlse, static_cast<bf16*>(a.dk),
                        static_cast<bf16*>(a.dv), a.N, BH, a.scale);
