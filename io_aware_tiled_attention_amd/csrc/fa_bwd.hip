@@ -336,12 +336,15 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
   const int mykey = kw0 + r32;
   const size_t head = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * G::R;
-  const rsrc_t rq = make_rsrc(Q + head, head_bytes);
-  const rsrc_t rk = make_rsrc(K + head, head_bytes);
-  const rsrc_t rv = make_rsrc(V + head, head_bytes);
-  const rsrc_t rdo = make_rsrc(dO + head, head_bytes);
-  const rsrc_t rnl = make_rsrc(nlse + (size_t)bh * N, (uint32_t)N * 4u);
-  const rsrc_t rdd = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
+  // copies into LDS are issued with lds_dma*_async and waited for at the
+  // end of each block (wait_vmem), so reads of the current block never wait
+  // for the next block's copy
+  const u32x4 rq = rsrc_words(Q + head, head_bytes);
+  const u32x4 rk = rsrc_words(K + head, head_bytes);
+  const u32x4 rv = rsrc_words(V + head, head_bytes);
+  const u32x4 rdo = rsrc_words(dO + head, head_bytes);
+  const u32x4 rnl = rsrc_words(nlse + (size_t)bh * N, (uint32_t)N * 4u);
+  const u32x4 rdd = rsrc_words(dsum + (size_t)bh * N, (uint32_t)N * 4u);
   const float kfac = X::factor(scale);
 
   // Loop-invariant per-lane LDS offsets.  The swizzle depends on the row
@@ -375,17 +378,17 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
 
   auto load_block = [&](int q0b, int st) {
     lds_u8* sb = smem + st * C::STAGE;
-    tile_to_lds<bf16, D, BQ, kKvWaves>(rq, sb + C::Q0, q0b, w, lane);
-    tile_to_lds<bf16, D, BQ, kKvWaves>(rdo, sb + C::DO0, q0b, w, lane);
-    if (w == 0) lds_dma4(rnl, sb + C::NL0, (q0b + lane) * 4);
-    if (w == 1) lds_dma4(rdd, sb + C::DD0, (q0b + lane) * 4);
+    tile_to_lds_async<bf16, D, BQ, kKvWaves>(rq, sb + C::Q0, q0b, w, lane);
+    tile_to_lds_async<bf16, D, BQ, kKvWaves>(rdo, sb + C::DO0, q0b, w, lane);
+    if (w == 0) lds_dma4_async(rnl, sb + C::NL0, (q0b + lane) * 4);
+    if (w == 1) lds_dma4_async(rdd, sb + C::DD0, (q0b + lane) * 4);
   };
 
   const int q_begin = CAUSAL ? k0 : 0;
   const int nblocks = (N - q_begin + BQ - 1) / BQ;
 
-  tile_to_lds<bf16, D, kBwdBK, kKvWaves>(rk, smem + C::KOFF, k0, w, lane);
-  tile_to_lds<bf16, D, kBwdBK, kKvWaves>(rv, smem + C::VOFF, k0, w, lane);
+  tile_to_lds_async<bf16, D, kBwdBK, kKvWaves>(rk, smem + C::KOFF, k0, w, lane);
+  tile_to_lds_async<bf16, D, kBwdBK, kKvWaves>(rv, smem + C::VOFF, k0, w, lane);
   load_block(q_begin, 0);
   wait_vmem();
   __syncthreads();
@@ -680,10 +683,219 @@ void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
                 acc[db][4 * a + 1] * scale, acc[db][4 * a + 2] * scale, acc[db][4 * a + 3] * scale);
 }
 
+// bf16 dQ: the same sweep with every LDS address a per-lane offset computed
+// once plus a compile-time constant (static LDS, the tile loop unrolled over
+// the two staging buffers), masking only on the tiles that cross the diagonal
+// or the end of the sequence, and operand reads issued one product ahead.
+// The two 32-key halves of a tile are processed one after the other so that
+// the first half's dS is already packed to bf16 while the second half's
+// products run.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kDqThreads, 2)
+void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                           const bf16* __restrict__ dO, const float* __restrict__ dsum,
+                           const float* __restrict__ nlse, bf16* __restrict__ dQ, int N, int BH, int n_qtiles,
+                           float scale) {
+  using M = Mfma<bf16>;
+  using G = Tile<bf16, D>;
+  using X = ExpDomain<bf16>;
+  using Frag = M::Frag;
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  constexpr int KPL = M::KPL, KC = M::KC;
+  constexpr int NKB = kDqBC / 32;
+  constexpr int NDB = D / 32, NC = D / KC;
+  constexpr int TILE = kDqBC * G::R;
+  // [K st0][K st1][V st0][V st1]
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[4 * TILE];
+  lds_u8* smem = (lds_u8*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int g = lane >> 5;
+  const int r32 = lane & 31;
+
+  const int bh = blockIdx.x % BH;
+  int qt = blockIdx.x / BH;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;         // longest first
+  const int q0 = qt * kDqBR;
+  const size_t head = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * G::R;
+  const rsrc_t rq = make_rsrc(Q + head, head_bytes);
+  // K/V tiles are copied with lds_dma16_async and waited for at the end of
+  // each tile (wait_vmem), so reads of tile j never wait for tile j+1's copy
+  const u32x4 rk = rsrc_words(K + head, head_bytes);
+  const u32x4 rv = rsrc_words(V + head, head_bytes);
+  const rsrc_t rdo = make_rsrc(dO + head, head_bytes);
+  const int qw0 = q0 + w * kDqQW;
+  const int myq = qw0 + r32;
+  const float kfac = X::factor(scale);
+
+  // Q^T and dO^T as B operands (column = query, KPL d-values of group g);
+  // this lane's lse (in the exponent domain) and D are scalars.
+  Frag qf[NC], dof[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int off = myq * G::R + (c * KC + g * KPL) * 2;
+    qf[c] = M::load(rq, off);
+    dof[c] = M::load(rdo, off);
+  }
+  const rsrc_t rnl = make_rsrc(nlse + (size_t)bh * N, (uint32_t)N * 4u);
+  const rsrc_t rdd = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
+  const float nl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rnl, myq * 4, 0, 0));
+  const float dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdd, myq * 4, 0, 0));
+
+  // Loop-invariant per-lane LDS offsets (the swizzle depends on the row
+  // modulo 16 only): ka[c] = row r32, k-chunk c of a tile; tk[db][e] = the
+  // transposed reads of rows 4g + (j>>2) + 8e, columns db*32 + 16h + 4(j&3).
+  int ka[NC], tk[NDB][2];
+  {
+    const int j = lane & 15, h = (lane >> 4) & 1;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) ka[c] = G::off(r32, c * KC + g * KPL);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) tk[db][e] = G::off(4 * g + (j >> 2) + 8 * e, db * 32 + 16 * h + 4 * (j & 3));
+  }
+
+  const int kv_end = CAUSAL ? min(N, q0 + kDqBR) : N;
+  const int ntiles = (kv_end + kDqBC - 1) / kDqBC;
+  const int wave_last = CAUSAL ? min(ntiles - 1, (qw0 + kDqQW - 1) / kDqBC) : ntiles - 1;
+
+  auto load_tile = [&](int j, int st) {
+    tile_to_lds_async<bf16, D, kDqBC, kDqWaves>(rk, smem + st * TILE, j * kDqBC, w, lane);
+    tile_to_lds_async<bf16, D, kDqBC, kDqWaves>(rv, smem + (2 + st) * TILE, j * kDqBC, w, lane);
+  };
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  load_tile(0, 0);
+  wait_vmem();
+  __syncthreads();
+
+  auto tile = [&](int j, auto st_c, auto masked_c) {
+    constexpr int ST = decltype(st_c)::value;
+    constexpr bool MASKED = decltype(masked_c)::value;
+    constexpr int KB = ST * TILE, VB = (2 + ST) * TILE;
+    const int kv0 = j * kDqBC;
+    if (j + 1 < ntiles) load_tile(j + 1, ST ^ 1);
+    if (!MASKED || j <= wave_last) {
+      bool msk = false;
+      int last = 0;
+      if constexpr (MASKED) {
+        msk = (CAUSAL && kv0 + kDqBC - 1 > qw0) || (kv0 + kDqBC > N);
+        last = CAUSAL ? min(N - 1, myq) : N - 1;   // keys allowed: key <= last
+      }
+      // S^T = K Q^T and dP^T = V dO^T for the 32 keys of half kb: rows = keys,
+      // column = this lane's query; operand reads run one product ahead.
+      auto sdp = [&](int kb, f32x16& s, f32x16& dp) {
+        s = f32x16{};
+        dp = f32x16{};
+        Frag fk[2], fv[2];
+        fk[0] = M::lds(smem + KB + kb * 32 * G::R + ka[0]);
+        fv[0] = M::lds(smem + VB + kb * 32 * G::R + ka[0]);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int cur = c & 1;
+          if (c + 1 < NC) {
+            fk[cur ^ 1] = M::lds(smem + KB + kb * 32 * G::R + ka[c + 1]);
+            fv[cur ^ 1] = M::lds(smem + VB + kb * 32 * G::R + ka[c + 1]);
+          }
+          s = M::mma(fk[cur], qf[c], s);
+          dp = M::mma(fv[cur], dof[c], dp);
+        }
+      };
+      // P = ex(S*factor - lse) (masked scores are -inf and factor > 0, so
+      // P = 0 there), dS = P (dP - D), packed to bf16 B fragments.
+      auto softmax = [&](int kb, f32x16& s, f32x16& dp, Frag* ds) {
+        if constexpr (MASKED) {
+          if (msk) {
+            const int lim = last - (kv0 + kb * 32 + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = (acc_row(i, 0) > lim) ? kNegInf : s[i];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = X::ex(__builtin_fmaf(s[i], kfac, nl));
+          dp[i] = p * (dp[i] - dd);
+        }
+        ds[0] = M::pack(dp, 0);
+        ds[1] = M::pack(dp, 1);
+      };
+      // dQ^T += K^T dS^T: K^T through the transpose read (A operand), dS^T
+      // straight from registers (B operand).
+      auto tr = [&](int kb, int t, int db) {
+        union { s16x4 h[2]; Frag f; } u;
+        const int base = KB + (kb * 32 + 16 * t) * G::R;
+        u.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + base + tk[db][0]));
+        u.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + base + tk[db][1]));
+        return u.f;
+      };
+      auto dq_mma = [&](int kb, const Frag* ds) {
+        Frag fa[2];
+        fa[0] = tr(kb, 0, 0);
+#pragma unroll
+        for (int n = 0; n < 2 * NDB; ++n) {
+          const int cur = n & 1;
+          if (n + 1 < 2 * NDB) fa[cur ^ 1] = tr(kb, (n + 1) / NDB, (n + 1) % NDB);
+          acc[n % NDB] = M::mma(fa[cur], ds[n / NDB], acc[n % NDB]);
+        }
+      };
+      Frag ds[NKB][2];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        f32x16 st, dpt;
+        sdp(kb, st, dpt);
+        softmax(kb, st, dpt, ds[kb]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) dq_mma(kb, ds[kb]);
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using Msk = std::integral_constant<bool, true>;
+  using NoMsk = std::integral_constant<bool, false>;
+  // Leading tiles that no wave needs to mask: keys below the workgroup's
+  // first query (causal), or all whole tiles (non-causal).
+  const int n_plain = CAUSAL ? min(ntiles, q0 / kDqBC) : N / kDqBC;
+  int j = 0;
+  for (; j + 1 < n_plain; j += 2) {
+    tile(j, S0{}, NoMsk{});
+    tile(j + 1, S1{}, NoMsk{});
+  }
+  if (j < n_plain) {
+    tile(j, S0{}, NoMsk{});
+    ++j;
+  }
+  for (; j < ntiles; ++j) {
+    if (j & 1) tile(j, S1{}, Msk{});
+    else tile(j, S0{}, Msk{});
+  }
+
+  // dQ = scale * acc; lane holds query myq, d = db*32 + acc_row(i, g).
+  const rsrc_t rdq = make_rsrc(dQ + head, head_bytes);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      store4<bf16>(rdq, myq * G::R + (db * 32 + 8 * a + 4 * g) * 2, acc[db][4 * a] * scale,
+                   acc[db][4 * a + 1] * scale, acc[db][4 * a + 2] * scale, acc[db][4 * a + 3] * scale);
+}
+
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   const int BH = a.B * a.H;
   const size_t rows = (size_t)BH * a.N;
+  const int n_ktiles = (a.N + kBwdBK - 1) / kBwdBK;
+  const int n_qtiles = (a.N + kDqBR - 1) / kDqBR;
   if (stages & kStagePre) {
     constexpr int RPB = 256 / (D / (16 / (int)sizeof(T)));
     const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
@@ -692,39 +904,42 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if ((stages & kStageDkDv) && sizeof(T) == 2) {
-    auto kern = fa_bwd_dkdv_bf16_kernel<D, CAUSAL>;
-    const int n_ktiles = (a.N + kBwdBK - 1) / kBwdBK;
-    hipLaunchKernelGGL(kern, dim3(n_ktiles * BH), dim3(kKvThreads), 0, stream,
-                       static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
-                       static_cast<const bf16*>(a.dout), a.dsum, a.nlse, static_cast<bf16*>(a.dk),
-                       static_cast<bf16*>(a.dv), a.N, BH, a.scale);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  } else if (stages & kStageDkDv) {
-    using C = BwdCfg<T, D>;
-    auto kern = fa_bwd_dkdv_kernel<T, D, CAUSAL>;
-    static const hipError_t attr_err =
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::BYTES);
-    if (attr_err != hipSuccess) return attr_err;
-    const int n_ktiles = (a.N + kBwdBK - 1) / kBwdBK;
-    hipLaunchKernelGGL(kern, dim3(n_ktiles * BH), dim3(kBwdThreads), C::BYTES, stream,
-                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                       static_cast<const T*>(a.dout), a.dsum, a.nlse, static_cast<T*>(a.dk),
-                       static_cast<T*>(a.dv), a.N, BH, a.scale);
+  if (stages & kStageDkDv) {
+    if constexpr (sizeof(T) == 2) {
+      hipLaunchKernelGGL((fa_bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3(n_ktiles * BH), dim3(kKvThreads), 0, stream,
+                         static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
+                         static_cast<const bf16*>(a.dout), a.dsum, a.nlse, static_cast<bf16*>(a.dk),
+                         static_cast<bf16*>(a.dv), a.N, BH, a.scale);
+    } else {
+      using C = BwdCfg<T, D>;
+      auto kern = fa_bwd_dkdv_kernel<T, D, CAUSAL>;
+      static const hipError_t attr_err =
+          hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::BYTES);
+      if (attr_err != hipSuccess) return attr_err;
+      hipLaunchKernelGGL(kern, dim3(n_ktiles * BH), dim3(kBwdThreads), C::BYTES, stream,
+                         static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                         static_cast<const T*>(a.dout), a.dsum, a.nlse, static_cast<T*>(a.dk),
+                         static_cast<T*>(a.dv), a.N, BH, a.scale);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & kStageDq) {
-    constexpr int bytes = 4 * kDqBC * D * (int)sizeof(T);
-    auto kern = fa_bwd_dq_kernel<T, D, CAUSAL>;
-    static const hipError_t attr_err =
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (attr_err != hipSuccess) return attr_err;
-    const int n_qtiles = (a.N + kDqBR - 1) / kDqBR;
-    hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(kDqThreads), bytes, stream, static_cast<const T*>(a.q),
-                       static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<const T*>(a.dout),
-                       a.dsum, a.nlse, static_cast<T*>(a.dq), a.N, BH, n_qtiles, a.scale);
+    if constexpr (sizeof(T) == 2) {
+      hipLaunchKernelGGL((fa_bwd_dq_bf16_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(kDqThreads), 0, stream,
+                         static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
+                         static_cast<const bf16*>(a.dout), a.dsum, a.nlse, static_cast<bf16*>(a.dq), a.N, BH,
+                         n_qtiles, a.scale);
+    } else {
+      constexpr int bytes = 4 * kDqBC * D * (int)sizeof(T);
+      auto kern = fa_bwd_dq_kernel<T, D, CAUSAL>;
+      static const hipError_t attr_err =
+          hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      if (attr_err != hipSuccess) return attr_err;
+      hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(kDqThreads), bytes, stream, static_cast<const T*>(a.q),
+                         static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<const T*>(a.dout),
+                         a.dsum, a.nlse, static_cast<T*>(a.dq), a.N, BH, n_qtiles, a.scale);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -127,6 +127,26 @@ __device__ __forceinline__ void lds_dma4(rsrc_t src, lds_u8* dst, int voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)dst, 4, voff, 0, 0, 0);
 }
 
+// The same global -> LDS copy issued through inline assembly, on a buffer
+// descriptor held as four words.  The compiler does not see this LDS write,
+// so it never makes later LDS reads wait for it: the caller waits itself
+// (wait_vmem) before the copied rows are read.  M0 holds the LDS address;
+// one wait state separates its write from the copy.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  return u32x4{(unsigned)a, (unsigned)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+__device__ __forceinline__ void lds_dma16_async(u32x4 src, const lds_u8* dst, int voff) {
+  const unsigned m = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m), "v"(voff), "s"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4_async(u32x4 src, const lds_u8* dst, int voff) {
+  const unsigned m = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(m), "v"(voff), "s"(src) : "memory", "m0");
+}
+
 // Copy rows [row0, row0 + ROWS) of one head's [N, D] tensor (buffer `src`)
 // into an LDS tile, spread over NW waves: each wave moves 1 KiB per
 // instruction, lane i landing at byte 16*i of the wave's segment.  Rows past
@@ -143,6 +163,22 @@ __device__ __forceinline__ void tile_to_lds(rsrc_t src, lds_u8* tile, int row0, 
     const int row = o / G::R;
     const int chunk = ((o % G::R) >> 4) ^ G::swz(row);
     lds_dma16(src, tile + s * 1024, (row0 + row) * G::R + chunk * 16);
+  }
+}
+
+// tile_to_lds through lds_dma16_async (see there for the waiting rule).
+template <typename T, int D, int ROWS, int NW>
+__device__ __forceinline__ void tile_to_lds_async(u32x4 src, lds_u8* tile, int row0, int w, int lane) {
+  using G = Tile<T, D>;
+  constexpr int SEGS = ROWS * G::R / 1024;
+  static_assert(SEGS % NW == 0, "tile must split evenly over the waves");
+#pragma unroll
+  for (int r = 0; r < SEGS / NW; ++r) {
+    const int s = w * (SEGS / NW) + r;
+    const int o = s * 1024 + lane * 16;
+    const int row = o / G::R;
+    const int chunk = ((o % G::R) >> 4) ^ G::swz(row);
+    lds_dma16_async(src, tile + s * 1024, (row0 + row) * G::R + chunk * 16);
   }
 }
 
