@@ -156,9 +156,10 @@ def kernel_table(p, avg):
         out[name] = {"kernel": kernel, "ms": avg[name], "flops": flops, "tflops": flops / avg[name] * 1e-9,
                      "frac_peak": flops / avg[name] * 1e-9 / PEAK_BF16_TFLOPS}
 
+    sfx = "_bf16" if p.dtype == "bf16" else ""     # bf16 has its own backward kernels
     mm("fwd", "fa_fwd_kernel", fwd_f)
-    mm("bwd_dkdv", "fa_bwd_dkdv_kernel", 4 * unit)
-    mm("bwd_dq", "fa_bwd_dq_kernel", 3 * unit)
+    mm("bwd_dkdv", f"fa_bwd_dkdv{sfx}_kernel", 4 * unit)
+    mm("bwd_dq", f"fa_bwd_dq{sfx}_kernel", 3 * unit)
     pre_bytes = 2 * tens + 3 * rows * 4                        # read O, dO, lse; write D, -lse
     out["bwd_pre"] = {"kernel": "fa_bwd_pre_kernel", "ms": avg["bwd_pre"], "bytes": pre_bytes,
                       "gbs": pre_bytes / avg["bwd_pre"] * 1e-6}
