@@ -270,9 +270,10 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
 // ---------------------------------------------------------------- 2b. dK, dV (bf16)
 // Eight waves over 128 keys: waves w and w + 4 own the same 32 keys (slice
 // w % 4) and take the first and the second 32-row query sub-block of every
-// 64-row block, so each SIMD runs two waves.  K and V stay resident in LDS
-// (their B-operand fragments are read per product instead of held in
-// registers), which is what makes two waves fit.  Every LDS address is a
+// 64-row block, so each SIMD runs two waves.  K and V stay resident in LDS;
+// each wave holds its K slice as B fragments in registers (read once) and
+// reads its V fragments per block -- holding both would not leave room for
+// two waves per SIMD.  Every LDS address is a
 // per-lane offset computed once plus a compile-time constant: the block loop
 // is unrolled over the two staging buffers, and blocks that cross no diagonal
 // and no end of the sequence run a body without any masking.  At the end the
@@ -392,6 +393,9 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
   load_block(q_begin, 0);
   wait_vmem();
   __syncthreads();
+  Frag kf[NC];   // this wave's K slice as B fragments, read once
+#pragma unroll
+  for (int c = 0; c < NC; ++c) kf[c] = M::lds(smem + ka[c]);
 
   // One 64-row query block from staging buffer ST; MASKED also handles the
   // causal diagonal and keys past the end of the sequence.
@@ -410,10 +414,9 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
       const lds_u8* sb = smem + ST * C::STAGE;
       // S = Q K^T and dP = dO V^T: rows = queries, column = this lane's key.
       f32x16 s = f32x16{}, dp = f32x16{};
-      Frag fq[2], fd[2], fk[2], fv[2];
+      Frag fq[2], fd[2], fv[2];
       fq[0] = M::lds(sb + C::Q0 + qa[0]);
       fd[0] = M::lds(sb + C::DO0 + qa[0]);
-      fk[0] = M::lds(smem + ka[0]);
       fv[0] = M::lds(smem + ka[0] + C::KTILE);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -421,10 +424,9 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
         if (c + 1 < NC) {
           fq[cur ^ 1] = M::lds(sb + C::Q0 + qa[c + 1]);
           fd[cur ^ 1] = M::lds(sb + C::DO0 + qa[c + 1]);
-          fk[cur ^ 1] = M::lds(smem + ka[c + 1]);
           fv[cur ^ 1] = M::lds(smem + ka[c + 1] + C::KTILE);
         }
-        s = M::mma(fq[cur], fk[cur], s);
+        s = M::mma(fq[cur], kf[c], s);
         dp = M::mma(fd[cur], fv[cur], dp);
         __builtin_amdgcn_sched_barrier(0);   // keep the reads one step ahead
       }
