@@ -31,6 +31,10 @@ Sources (page title -> part used):
 * "Overview of Flash Attention series", section *Backward Pass of
   flashattention*: dV = P^T dO, dP = dO V^T, D_i = P_i:^T dP_i: = do_i^T o_i,
   dS = P o (dP - D), dq_i = sum_j dS_ij k_j, dk_j = sum_i dS_ij q_i.
+* "Overview of Flash Attention series", section *Block-sparse
+  Flashattention*: attention under a mask M in {0,1}^{N x N} whose nonzero
+  entries come in blocks of a coarser block mask, computed by skipping the
+  zero blocks.
 
 Readings taken where the pages are silent or disagree (each one is listed in
 the design notes of the repository):
@@ -44,6 +48,11 @@ the design notes of the repository):
   the unmasked j, natural log, of the *scaled* scores.
 * In the coreui worked example the split is along keys (what the primer calls
   T_c / B_c); a block holds keys [j*Bc, (j+1)*Bc), end exclusive.
+* Block-sparse attention: the page writes softmax(S o 1_M) with masked
+  entries set to 0, but its algorithm skips the zero blocks, so they carry no
+  weight at all.  Reading: masked entries are excluded (-inf), as for the
+  causal mask.  A row with no remaining entry has O = 0 and lse = -inf (the
+  empty sum).
 
 Parity status: every public function here is pinned by tests/test_oracle.py
 (page worked example, closed forms, library cross-checks, brute force,
@@ -70,6 +79,9 @@ __all__ = [
     "blockwise_forward_head",
     "brute_force_forward_head",
     "finite_difference_grads",
+    "expand_block_mask",
+    "forward_block_sparse_head",
+    "forward_block_sparse",
 ]
 
 
@@ -315,14 +327,16 @@ def blockwise_forward_head(q, k, v, block_q: int, block_k: int, causal: bool = F
     return o_all, lse_all
 
 
-def brute_force_forward_head(q, k, v, causal: bool = False, scale: Optional[float] = None):
+def brute_force_forward_head(q, k, v, causal: bool = False, scale: Optional[float] = None, allowed=None):
     """Attention by scalar loops with math.exp, for tiny problems only.
 
     Each output row o_i = sum_j exp(s_ij) v_j / sum_j exp(s_ij) with
     s_ij = scale * sum_c q_ic k_jc ("Overview of Flash Attention series",
     Forward Pass of flashattention: the normaliser L_i and o_i written per
     row), evaluated with a max shift for range.  No numpy arithmetic, so it
-    shares no code path with :func:`forward_head`.
+    shares no code path with :func:`forward_head`.  ``allowed(i, j)``, if
+    given, further restricts the keys of row i (block-sparse masks); a row
+    with no key left gets o_i = 0 and lse_i = -inf.
     """
     q = [[float(x) for x in row] for row in np.asarray(q)]
     k = [[float(x) for x in row] for row in np.asarray(k)]
@@ -334,7 +348,11 @@ def brute_force_forward_head(q, k, v, causal: bool = False, scale: Optional[floa
     o_rows: List[List[float]] = []
     lse_rows: List[float] = []
     for i in range(n_q):
-        keys = [j for j in range(len(k)) if not (causal and j > i)]
+        keys = [j for j in range(len(k)) if not (causal and j > i) and (allowed is None or allowed(i, j))]
+        if not keys:
+            o_rows.append([0.0] * dv)
+            lse_rows.append(-math.inf)
+            continue
         s = [scale * math.fsum(q[i][c] * k[j][c] for c in range(d)) for j in keys]
         mx = max(s)
         w = [math.exp(x - mx) for x in s]
@@ -373,3 +391,64 @@ def finite_difference_grads(q, k, v, g, causal: bool = False, scale: Optional[fl
             gx[idx] = (up - dn) / (2.0 * h)
         grads.append(gx)
     return tuple(grads)
+
+
+def expand_block_mask(block_mask, n_q: int, n_k: int, block_q: int, block_k: int) -> np.ndarray:
+    """Element mask of a block mask: M[r, c] = B[r // block_q, c // block_k].
+
+    "Overview of Flash Attention series", Block-sparse Flashattention: the
+    mask M in {0,1}^{N x N} is constant on blocks of block_q query rows by
+    block_k keys, and B says which blocks are kept.  Returns a bool [n_q, n_k].
+    """
+    b = np.asarray(block_mask) != 0
+    rows = np.arange(n_q) // block_q
+    cols = np.arange(n_k) // block_k
+    return b[rows[:, None], cols[None, :]]
+
+
+def forward_block_sparse_head(q, k, v, block_mask, block_q: int, block_k: int, causal: bool = False,
+                              scale: Optional[float] = None):
+    """Block-sparse attention for one head: returns (O, lse).
+
+    S = scale Q K^T; entries outside the expanded block mask (and, if causal,
+    keys after the query) are excluded, P = softmax of what remains in each
+    row, O = P V, lse = m + ln l ("Overview of Flash Attention series",
+    Block-sparse Flashattention, with masked entries excluded as the
+    block-skipping algorithm does).  A row with no remaining entry has
+    O = 0 and lse = -inf.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    s = scores(q, k, scale, causal)
+    keep = expand_block_mask(block_mask, q.shape[0], k.shape[0], block_q, block_k)
+    s = np.where(keep, s, -np.inf)
+    empty = np.all(np.isneginf(s), axis=-1)
+    o = np.zeros((q.shape[0], v.shape[1]))
+    lse = np.full(q.shape[0], -np.inf)
+    if np.any(~empty):
+        p, m, l = softmax_stats(s[~empty])
+        o[~empty] = p @ v
+        lse[~empty] = m + np.log(l)
+    return o, lse
+
+
+def forward_block_sparse(q, k, v, block_mask, block_q: int, block_k: int, causal: bool = False,
+                         scale: Optional[float] = None):
+    """Block-sparse attention over [B, H, N, d] inputs, one head at a time.
+
+    ``block_mask`` is [Hm, ceil(N / block_q), ceil(N / block_k)] with Hm = 1
+    (one mask for every head) or Hm = H (one per head, shared by the batch).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    bm = np.asarray(block_mask)
+    B, H = q.shape[0], q.shape[1]
+    o = np.empty(q.shape[:-1] + (v.shape[-1],))
+    lse = np.empty(q.shape[:-1])
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h] = forward_block_sparse_head(q[b, h], k[b, h], v[b, h], bm[h if bm.shape[0] > 1 else 0],
+                                                           block_q, block_k, causal, scale)
+    return o, lse

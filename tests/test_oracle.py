@@ -354,3 +354,104 @@ def test_pins_catch_planted_forward_mistakes(worked):
 
     np.testing.assert_allclose(recurrence(+1), o_page, rtol=1e-14)
     assert not np.allclose(recurrence(-1), o_page, rtol=1e-6)
+
+
+# ---------------------------------------------------------------- block-sparse attention
+# "Overview of Flash Attention series", Block-sparse Flashattention: a mask
+# that is constant on blocks; zero blocks are skipped (no weight at all).
+
+def _block_mask(tq, tk, density, seed):
+    return (np.random.default_rng(seed).random((tq, tk)) < density).astype(np.uint8)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_all_ones_is_dense(causal):
+    n, d = 40, 8
+    q, k, v = (_rand((n, d), 700 + i) for i in range(3))
+    ones = np.ones((3, 5), dtype=np.uint8)          # block_q = 16, block_k = 8 (ragged last blocks)
+    o, lse = ref.forward_block_sparse_head(q, k, v, ones, 16, 8, causal, 0.4)
+    o_d, lse_d = ref.forward_head(q, k, v, causal, 0.4)
+    np.testing.assert_allclose(o, o_d, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_d, rtol=1e-13)
+
+
+@pytest.mark.parametrize("n,bq,bk,causal", [(12, 4, 3, False), (13, 4, 2, True), (9, 2, 4, False), (16, 8, 8, True)])
+def test_block_sparse_matches_brute_force(n, bq, bk, causal):
+    d = 3
+    q, k, v = (_rand((n, d), 710 + i) for i in range(3))
+    bm = _block_mask(-(-n // bq), -(-n // bk), 0.5, 77 + n)
+    bm[0, 0] = 1
+    o, lse = ref.forward_block_sparse_head(q, k, v, bm, bq, bk, causal, 0.7)
+    o_b, lse_b = ref.brute_force_forward_head(q, k, v, causal, 0.7, allowed=lambda i, j: bm[i // bq][j // bk] != 0)
+    np.testing.assert_allclose(o, o_b, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_b, rtol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_matches_torch_sdpa_with_boolean_mask(causal):
+    n, d, bq, bk = 48, 16, 16, 8
+    q, k, v = (_rand((2, 3, n, d), 720 + i) for i in range(3))
+    bm = np.stack([_block_mask(3, 6, 0.45, 90 + h) for h in range(3)])
+    bm[:, :, 0] = 1                                  # every row keeps key block 0 (row 0 keeps key 0 when causal)
+    o, lse = ref.forward_block_sparse(q, k, v, bm, bq, bk, causal, 0.3)
+    keep = np.stack([ref.expand_block_mask(bm[h], n, n, bq, bk) for h in range(3)])   # torch's mask: True = attend
+    if causal:
+        keep = keep & np.tril(np.ones((n, n), dtype=bool))
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    o_t = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(keep)[None], scale=0.3)
+    np.testing.assert_allclose(o, o_t.numpy(), rtol=1e-12, atol=1e-13)
+    s = 0.3 * np.einsum("bhid,bhjd->bhij", q, k)
+    lse_s = scipy.special.logsumexp(np.where(keep[None], s, -np.inf), axis=-1)
+    np.testing.assert_allclose(lse, lse_s, rtol=1e-12)
+
+
+def test_block_sparse_single_key_block_is_attention_on_that_slice():
+    """Keeping only key block c of a row block gives dense attention over the
+    keys of that block alone -- fails on a wrong block-to-index mapping."""
+    n, d, bq, bk = 32, 8, 8, 4
+    q, k, v = (_rand((n, d), 730 + i) for i in range(3))
+    bm = np.zeros((4, 8), dtype=np.uint8)
+    for r in range(4):
+        bm[r, (3 * r + 1) % 8] = 1
+    o, lse = ref.forward_block_sparse_head(q, k, v, bm, bq, bk, False, 0.5)
+    for r in range(4):
+        c = (3 * r + 1) % 8
+        rows, cols = slice(r * bq, (r + 1) * bq), slice(c * bk, (c + 1) * bk)
+        o_s, lse_s = ref.forward_head(q[rows], k[cols], v[cols], False, 0.5)
+        np.testing.assert_allclose(o[rows], o_s, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse[rows], lse_s, rtol=1e-13)
+
+
+def test_block_sparse_empty_row_is_zero_with_minus_inf_lse():
+    n, d = 16, 4
+    q, k, v = (_rand((n, d), 740 + i) for i in range(3))
+    bm = np.array([[1, 0], [0, 0], [0, 1], [1, 1]], dtype=np.uint8)   # block_q = 4, block_k = 8
+    o, lse = ref.forward_block_sparse_head(q, k, v, bm, 4, 8, False, 0.5)
+    assert np.all(o[4:8] == 0.0) and np.all(np.isneginf(lse[4:8]))
+    assert np.all(np.isfinite(lse[:4])) and np.all(np.isfinite(lse[8:]))
+    # causal: row block 2 keeps only key block 1 (keys 8..15), so rows 8..15 see keys 8..row
+    o_c, lse_c = ref.forward_block_sparse_head(q, k, v, bm, 4, 8, True, 0.5)
+    o_r, lse_r = ref.forward_head(q[8:12], k[8:16], v[8:16], True, 0.5)
+    np.testing.assert_allclose(o_c[8:12], o_r, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse_c[8:12], lse_r, rtol=1e-13)
+
+
+def test_block_sparse_pins_catch_planted_mistakes():
+    """A transposed block mask or masked scores set to 0 instead of excluded
+    (the page's literal S o 1_M) both fail the brute-force pin."""
+    n, d, blk = 12, 3, 4
+    q, k, v = (_rand((n, d), 750 + i) for i in range(3))
+    bm = np.array([[1, 0, 1], [0, 1, 1], [1, 0, 0]], dtype=np.uint8)   # not symmetric
+    o_b, _ = ref.brute_force_forward_head(q, k, v, False, 0.7, allowed=lambda i, j: bm[i // blk][j // blk] != 0)
+
+    def zero_filled(q, k, v):
+        s = ref.scores(q, k, 0.7, False)
+        s = np.where(ref.expand_block_mask(bm, n, n, blk, blk), s, 0.0)
+        p, _, _ = ref.softmax_stats(s)
+        return p @ v
+
+    o_tr, _ = ref.forward_block_sparse_head(q, k, v, bm.T, blk, blk, False, 0.7)
+    assert not np.allclose(zero_filled(q, k, v), o_b, atol=1e-6)
+    assert not np.allclose(o_tr, o_b, atol=1e-6)
+    o_ok, _ = ref.forward_block_sparse_head(q, k, v, bm, blk, blk, False, 0.7)
+    np.testing.assert_allclose(o_ok, o_b, rtol=1e-12, atol=1e-13)
