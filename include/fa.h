@@ -64,7 +64,8 @@ enum fa_status {
   FA_ERR_SCALE = 5,     /* scale is NaN, infinite or negative */
   FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than fa_backward_workspace_size */
   FA_ERR_HIP = 7,       /* the HIP runtime reported an error at launch */
-  FA_ERR_ALIGN = 8      /* a tensor pointer is not 16-byte aligned */
+  FA_ERR_ALIGN = 8,     /* a tensor pointer is not 16-byte aligned */
+  FA_ERR_MASK = 9       /* block-sparse mask geometry invalid (see fa_forward_block_sparse) */
 };
 
 /*
@@ -80,6 +81,28 @@ enum fa_status {
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, int causal, float scale, int dtype,
                void* stream);
+
+/*
+ * Block-sparse forward pass ("Overview of Flash Attention series", section
+ * Block-sparse Flashattention): attention restricted by a mask that is
+ * constant on blocks of block_q query rows by block_k keys.  Masked entries
+ * carry no weight at all (the blocks are skipped, as the page's algorithm
+ * does; its formula S o 1_M is read as excluding them, like the causal mask).
+ *   block_mask: DEVICE pointer, uint8, contiguous
+ *     [mask_heads][ceil(N/block_q)][ceil(N/block_k)]; non-zero keeps a block.
+ *     mask_heads = 1 applies one mask to every (batch, head); mask_heads = H
+ *     gives head h the mask h, shared by the batch.  Read-only.
+ *   block_q: a positive multiple of 32; block_k: a positive multiple of 64.
+ *   N <= 65536.  Violations return FA_ERR_MASK.
+ *   causal != 0 additionally keeps key index <= query index.
+ * Everything else as fa_forward.  A query row that keeps no key gets O = 0
+ * and lse = -inf.  Key tiles masked out for a whole workgroup are neither
+ * read from memory nor computed, so the work and the K/V traffic scale with
+ * the kept fraction of blocks.
+ */
+int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const unsigned char* block_mask, int mask_heads, int block_q, int block_k,
+                            int B, int H, int N, int d, int causal, float scale, int dtype, void* stream);
 
 /*
  * Bytes of device workspace that fa_backward needs: two fp32 row statistics

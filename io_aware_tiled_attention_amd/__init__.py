@@ -8,6 +8,7 @@ contiguous [B, H, N, d] in float32 or bfloat16 on a ROCm device; lse is
 
     o, lse = forward(q, k, v, causal=True)
     dq, dk, dv = backward(q, k, v, o, do, lse, causal=True)
+    o, lse = forward_block_sparse(q, k, v, block_mask, block_q=128, block_k=64)
 """
 from __future__ import annotations
 
@@ -16,11 +17,12 @@ from typing import Optional, Tuple
 
 from . import _lib
 from ._lib import (FA_BF16, FA_F32, FaError, fa_backward, fa_backward_dkdv, fa_backward_dq,
-                   fa_backward_preprocess, fa_backward_workspace_size, fa_forward, fa_strerror)
+                   fa_backward_preprocess, fa_backward_workspace_size, fa_forward, fa_forward_block_sparse,
+                   fa_strerror)
 
-__all__ = ["forward", "backward", "workspace_size", "FaError", "FA_F32", "FA_BF16",
-           "fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_preprocess",
-           "fa_backward_dkdv", "fa_backward_dq", "fa_strerror", "load_library",
+__all__ = ["forward", "forward_block_sparse", "backward", "workspace_size", "FaError", "FA_F32", "FA_BF16",
+           "fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_size",
+           "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_strerror", "load_library",
            "backward_stages"]
 
 
@@ -77,6 +79,45 @@ def forward(q, k, v, causal: bool = False, scale: Optional[float] = None,
                     B, H, N, d, causal, scale, _dtype_code(q), _stream_ptr(q.device))
     if st != 0:
         raise FaError(st, "fa_forward")
+    return out, lse
+
+
+def forward_block_sparse(q, k, v, block_mask, block_q: int, block_k: int, causal: bool = False,
+                         scale: Optional[float] = None, out=None, lse=None):
+    """Block-sparse attention: like :func:`forward`, with the keys of each row
+    restricted to the blocks that ``block_mask`` keeps.
+
+    block_mask: uint8 tensor [Hm, ceil(N / block_q), ceil(N / block_k)] on the
+    same device, Hm = 1 (every head) or H (per head, shared by the batch);
+    non-zero keeps a block of block_q query rows by block_k keys.  block_q must
+    be a multiple of 32 and block_k of 64.  Rows that keep no key get O = 0 and
+    lse = -inf.
+    """
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if q.device.type != "cuda":
+        raise ValueError("tensors must live on a ROCm device")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(name, t, q.shape, q.dtype, q.device)
+    if block_mask.dim() != 3:
+        raise ValueError("block_mask must be [Hm, ceil(N / block_q), ceil(N / block_k)]")
+    tq, tk = -(-N // block_q), -(-N // block_k)
+    _check("block_mask", block_mask, (block_mask.shape[0], tq, tk), torch.uint8, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check("out", out, q.shape, q.dtype, q.device)
+    _check("lse", lse, (B, H, N), torch.float32, q.device)
+    st = fa_forward_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                 block_mask.data_ptr(), block_mask.shape[0], block_q, block_k, B, H, N, d, causal,
+                                 scale, _dtype_code(q), _stream_ptr(q.device))
+    if st != 0:
+        raise FaError(st, "fa_forward_block_sparse")
     return out, lse
 
 

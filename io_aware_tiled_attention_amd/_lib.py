@@ -18,10 +18,10 @@ FA_F32 = 0
 FA_BF16 = 1
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_DTYPE",
-    5: "FA_ERR_SCALE", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ALIGN",
+    5: "FA_ERR_SCALE", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ALIGN", 9: "FA_ERR_MASK",
 }
-EXPORTED = ("fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_preprocess",
-            "fa_backward_dkdv", "fa_backward_dq", "fa_strerror")
+EXPORTED = ("fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_size",
+            "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_strerror")
 
 _lock = threading.Lock()
 _lib = None
@@ -49,6 +49,8 @@ def load() -> ctypes.CDLL:
         vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
         lib.fa_forward.restype = i
+        lib.fa_forward_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp]
+        lib.fa_forward_block_sparse.restype = i
         lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
         lib.fa_backward.restype = i
         lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
@@ -67,6 +69,12 @@ def load() -> ctypes.CDLL:
 
 def fa_forward(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream) -> int:
     return load().fa_forward(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), dtype, stream)
+
+
+def fa_forward_block_sparse(q, k, v, o, lse, block_mask, mask_heads, block_q, block_k, B, H, N, d, causal,
+                            scale, dtype, stream) -> int:
+    return load().fa_forward_block_sparse(q, k, v, o, lse, block_mask, mask_heads, block_q, block_k, B, H, N, d,
+                                          int(causal), float(scale), dtype, stream)
 
 
 def fa_backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype,

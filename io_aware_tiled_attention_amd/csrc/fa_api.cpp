@@ -88,6 +88,22 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
   return hip_status(fa::launch_forward(a, static_cast<hipStream_t>(stream)));
 }
 
+int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const unsigned char* block_mask, int mask_heads, int block_q, int block_k, int B,
+                            int H, int N, int d, int causal, float scale, int dtype, void* stream) {
+  bool empty = false;
+  const int st = check_shape(B, H, N, d, dtype, scale, &empty);
+  if (st != FA_OK) return st;
+  if (block_q <= 0 || block_q % 32 != 0 || block_k <= 0 || block_k % 64 != 0 || N > fa::kSparseMaxN ||
+      (mask_heads != 1 && mask_heads != H))
+    return FA_ERR_MASK;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !block_mask) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal ? 1 : 0, dtype, scale, block_mask, mask_heads, block_q, block_k};
+  return hip_status(fa::launch_forward(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
   bool empty = false;
   if (check_shape(B, H, N, d, FA_BF16, 1.f, &empty) != FA_OK || empty) return 0;
@@ -132,6 +148,9 @@ const char* fa_strerror(int status) {
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_backward_workspace_size()";
     case FA_ERR_HIP: return "the HIP runtime reported an error at launch";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned (workspace: 256-byte)";
+    case FA_ERR_MASK:
+      return "invalid block mask geometry: mask_heads must be 1 or H, block_q a positive multiple of 32, "
+             "block_k a positive multiple of 64, and N at most 65536";
     default: return "unknown fa_status";
   }
 }

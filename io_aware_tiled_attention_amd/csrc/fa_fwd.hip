@@ -47,6 +47,10 @@ constexpr int kFwdQW = 32;                      // query rows per wave
 constexpr int kFwdBR = kFwdWaves * kFwdQW;      // query rows per workgroup
 constexpr int kFwdBC = 64;                      // keys per K/V tile
 constexpr int kFwdThreads = kFwdWaves * 64;
+// Block-sparse: the key tiles a workgroup visits are listed in LDS, at most
+// this many (N <= 64 * kFwdMaxTiles = 65536), with one bit per wave.
+constexpr int kFwdMaxTiles = 1024;
+constexpr int kFwdListBytes = 4096;   // u16 tile index + u8 wave bits per entry, 4 counters
 
 template <typename T, int D>
 struct FwdSmem {
@@ -57,10 +61,20 @@ struct FwdSmem {
   __device__ static lds_u8* v(lds_u8* base, int st) { return base + (2 + st) * TILE; }
 };
 
-template <typename T, int D, bool CAUSAL>
+// SPARSE: block-sparse attention ("Overview of Flash Attention series",
+// Block-sparse Flashattention).  mask[mh][qb][kb] != 0 keeps the block of
+// block_q query rows by block_k keys (mh = head if mask_heads > 1, else 0);
+// key tiles whose block is zero for every wave of the workgroup are neither
+// loaded nor computed, and a wave skips a loaded tile whose block is zero
+// for its own rows -- the causal tile skip generalised to a block mask.
+// block_q is a multiple of 32 (one mask row per wave) and block_k a multiple
+// of 64 (one mask column per tile), so no tile is partly masked by the block
+// mask.  A row that keeps no key gets O = 0 and lse = -inf.
+template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1)
 void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-                   T* __restrict__ O, float* __restrict__ LSE, int N, int BH, int n_qtiles, float scale) {
+                   T* __restrict__ O, float* __restrict__ LSE, int N, int BH, int n_qtiles, float scale,
+                   const unsigned char* __restrict__ mask, int H, int mask_heads, int block_q, int block_k) {
   using M = Mfma<T>;
   using L = FwdSmem<T, D>;
   using G = Tile<T, D>;
@@ -119,24 +133,92 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   float msub = kNegInf;    // exponent shift (running max of scaled scores, raised lazily)
   float l_run = 0.f;       // this lane's share of the running row sum, relative to msub
 
-  // Prologue: K0, V0 (and K1) resident; S_0 computed.
-  tile_to_lds<T, D, kFwdBC, kFwdWaves>(rk, L::k(smem, 0), 0, w, lane);
-  tile_to_lds<T, D, kFwdBC, kFwdWaves>(rv, L::v(smem, 0), 0, w, lane);
-  if (ntiles > 1) tile_to_lds<T, D, kFwdBC, kFwdWaves>(rk, L::k(smem, 1), kFwdBC, w, lane);
-  wait_vmem();
-  __syncthreads();
+  // The tiles this workgroup visits, in order: every tile up to kv_end
+  // (dense), or the listed ones (block-sparse).  tile_of(i) is the i-th
+  // visited tile, active(i) whether this wave computes it.
+  typedef __attribute__((address_space(3))) unsigned short lds_u16;
+  typedef __attribute__((address_space(3))) int lds_i32;
+  lds_u16* act = (lds_u16*)(smem + L::BYTES);
+  lds_u8* wbit = (lds_u8*)(act + kFwdMaxTiles);
+  int n_act = ntiles;
+  if constexpr (SPARSE) {
+    lds_i32* cnt = (lds_i32*)(wbit + kFwdMaxTiles);
+    const int tk_n = (N + block_k - 1) / block_k;
+    const int tq_n = (N + block_q - 1) / block_q;
+    const unsigned char* mrow = mask + (size_t)(mask_heads > 1 ? bh % H : 0) * tq_n * tk_n;
+    n_act = 0;
+    for (int base = 0; base < ntiles; base += kFwdThreads) {
+      const int j = base + tid;
+      unsigned bits = 0;
+      if (j < ntiles) {
+        const int kb = j * kFwdBC / block_k;
+#pragma unroll
+        for (int w2 = 0; w2 < kFwdWaves; ++w2) {
+          const int qw = q0 + w2 * kFwdQW;
+          const bool reach = qw < N && !(CAUSAL && j * kFwdBC > qw + kFwdQW - 1);
+          if (reach && mrow[(qw / block_q) * tk_n + kb] != 0) bits |= 1u << w2;
+        }
+      }
+      const unsigned long long bal = __builtin_amdgcn_ballot_w64(bits != 0);
+      if (lane == 0) cnt[w] = __builtin_popcountll(bal);
+      __syncthreads();
+      int off = 0, tot = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < kFwdWaves; ++w2) {
+        const int c = cnt[w2];
+        off += w2 < w ? c : 0;
+        tot += c;
+      }
+      if (bits) {
+        const int pos = n_act + off + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+        act[pos] = (unsigned short)j;
+        wbit[pos] = (unsigned char)bits;
+      }
+      n_act += tot;
+      __syncthreads();
+    }
+  } else {
+    (void)mask;
+    (void)H;
+    (void)mask_heads;
+    (void)block_q;
+    (void)block_k;
+  }
+  auto tile_of = [&](int i) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)act[i]);
+    else return i;
+  };
+  auto active = [&](int i) -> bool {
+    if constexpr (SPARSE) return (__builtin_amdgcn_readfirstlane((int)wbit[i]) >> w) & 1;
+    else return i <= wave_last;
+  };
 
+  // Prologue: K and V of the first visited tile (and K of the second)
+  // resident; its S computed.
   f32x16 s_cur[NKB], s_nxt[NKB];
-  compute_st(s_cur, L::k(smem, 0));
+  if (n_act > 0) {
+    tile_to_lds<T, D, kFwdBC, kFwdWaves>(rk, L::k(smem, 0), tile_of(0) * kFwdBC, w, lane);
+    tile_to_lds<T, D, kFwdBC, kFwdWaves>(rv, L::v(smem, 0), tile_of(0) * kFwdBC, w, lane);
+    if (n_act > 1) tile_to_lds<T, D, kFwdBC, kFwdWaves>(rk, L::k(smem, 1), tile_of(1) * kFwdBC, w, lane);
+    wait_vmem();
+    __syncthreads();
+    if (active(0)) compute_st(s_cur, L::k(smem, 0));
+    // iteration 0 refills K stage 0 (with the third tile): every wave must
+    // have read the first tile's K fragments first
+    __syncthreads();
+  }
 
-  for (int j = 0; j < ntiles; ++j) {
+  for (int it = 0; it < n_act; ++it) {
+    const int j = tile_of(it);
     const int kv0 = j * kFwdBC;
-    if (j + 2 < ntiles) tile_to_lds<T, D, kFwdBC, kFwdWaves>(rk, L::k(smem, j & 1), kv0 + 2 * kFwdBC, w, lane);
-    if (j + 1 < ntiles) tile_to_lds<T, D, kFwdBC, kFwdWaves>(rv, L::v(smem, (j + 1) & 1), kv0 + kFwdBC, w, lane);
-    // S_{j+1} goes to the matrix core first; the vector work below overlaps it.
-    if (j + 1 <= wave_last) compute_st(s_nxt, L::k(smem, (j + 1) & 1));
+    if (it + 2 < n_act)
+      tile_to_lds<T, D, kFwdBC, kFwdWaves>(rk, L::k(smem, it & 1), tile_of(it + 2) * kFwdBC, w, lane);
+    if (it + 1 < n_act)
+      tile_to_lds<T, D, kFwdBC, kFwdWaves>(rv, L::v(smem, (it + 1) & 1), tile_of(it + 1) * kFwdBC, w, lane);
+    // S of the next tile goes to the matrix core first; the vector work below overlaps it.
+    if (it + 1 < n_act && active(it + 1)) compute_st(s_nxt, L::k(smem, (it + 1) & 1));
 
-    if (j <= wave_last) {
+    if (active(it)) {
       const bool masked = (CAUSAL && kv0 + kFwdBC - 1 > qw0) || (kv0 + kFwdBC > N);
       if (masked) {
         // keys allowed for this lane: key <= min(N-1, myq) (causal) or key <= N-1
@@ -182,7 +264,7 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
       l_run += psum;
 
       // O^T += V^T P^T, with P^T straight from the registers of S^T.
-      const lds_u8* vs = L::v(smem, j & 1);
+      const lds_u8* vs = L::v(smem, it & 1);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -208,9 +290,11 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     for (int kb = 0; kb < NKB; ++kb) s_cur[kb] = s_nxt[kb];
   }
 
-  // Epilogue: O = O_acc / l (deferred normalisation), lse = shift + ln l.
+  // Epilogue: O = O_acc / l (deferred normalisation), lse = shift + ln l;
+  // a row that kept no key (block-sparse) gets O = 0 and lse = -inf.
   const float l_tot = pair_sum(l_run);
-  const float inv = 1.f / l_tot;
+  const bool no_key = !(l_tot > 0.f);
+  const float inv = no_key ? 0.f : 1.f / l_tot;
   const rsrc_t ro = make_rsrc(O + head, head_bytes);
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -222,25 +306,31 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     }
   // both lanes of a query pair write the same value
   const rsrc_t rl = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
-  const float lse = msub * X::kToNat + logf(l_tot);
+  const float lse = no_key ? kNegInf : msub * X::kToNat + logf(l_tot);
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, myq * 4, 0, 0);
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   using L = FwdSmem<T, D>;
-  auto kern = fa_fwd_kernel<T, D, CAUSAL>;
+  constexpr int bytes = L::BYTES + (SPARSE ? kFwdListBytes : 0);
+  auto kern = fa_fwd_kernel<T, D, CAUSAL, SPARSE>;
   // raise the dynamic-LDS limit once per instantiation (thread-safe static init)
   static const hipError_t attr_err =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (attr_err != hipSuccess) return attr_err;
   const int BH = a.B * a.H;
   const int n_qtiles = (a.N + kFwdBR - 1) / kFwdBR;
   const dim3 grid(n_qtiles * BH), block(kFwdThreads);
-  hipLaunchKernelGGL(kern, grid, block, L::BYTES, stream, static_cast<const T*>(a.q),
+  hipLaunchKernelGGL(kern, grid, block, bytes, stream, static_cast<const T*>(a.q),
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<T*>(a.o),
-                     a.lse, a.N, BH, n_qtiles, a.scale);
+                     a.lse, a.N, BH, n_qtiles, a.scale, a.mask, a.H, a.mask_heads, a.block_q, a.block_k);
   return hipGetLastError();
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_fwd_m(const FwdArgs& a, hipStream_t stream) {
+  return a.mask ? launch_fwd_t<T, D, CAUSAL, true>(a, stream) : launch_fwd_t<T, D, CAUSAL, false>(a, stream);
 }
 
 }  // namespace
@@ -248,11 +338,11 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream) {
   const bool c = a.causal != 0;
   if (a.dtype == kDtypeBF16) {
-    if (a.d == 64) return c ? launch_fwd_t<bf16, 64, true>(a, stream) : launch_fwd_t<bf16, 64, false>(a, stream);
-    return c ? launch_fwd_t<bf16, 128, true>(a, stream) : launch_fwd_t<bf16, 128, false>(a, stream);
+    if (a.d == 64) return c ? launch_fwd_m<bf16, 64, true>(a, stream) : launch_fwd_m<bf16, 64, false>(a, stream);
+    return c ? launch_fwd_m<bf16, 128, true>(a, stream) : launch_fwd_m<bf16, 128, false>(a, stream);
   }
-  if (a.d == 64) return c ? launch_fwd_t<float, 64, true>(a, stream) : launch_fwd_t<float, 64, false>(a, stream);
-  return c ? launch_fwd_t<float, 128, true>(a, stream) : launch_fwd_t<float, 128, false>(a, stream);
+  if (a.d == 64) return c ? launch_fwd_m<float, 64, true>(a, stream) : launch_fwd_m<float, 64, false>(a, stream);
+  return c ? launch_fwd_m<float, 128, true>(a, stream) : launch_fwd_m<float, 128, false>(a, stream);
 }
 
 }  // namespace fa

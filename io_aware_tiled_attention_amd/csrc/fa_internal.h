@@ -17,7 +17,12 @@ struct FwdArgs {
   float* lse;
   int B, H, N, d, causal, dtype;
   float scale;
+  // block-sparse forward only (mask == nullptr: dense)
+  const unsigned char* mask = nullptr;
+  int mask_heads = 0, block_q = 0, block_k = 0;
 };
+
+constexpr int kSparseMaxN = 65536;   // N limit of the block-sparse forward
 
 struct BwdArgs {
   const void* q;

@@ -64,8 +64,10 @@ def test_causal_16k_d128_stressed_sampled():
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("n", [1, 2, 63, 65, 129, 257])
+@pytest.mark.parametrize("n", [1, 2, 63, 65, 129, 257, 320, 448])
 def test_ragged_lengths(n, causal, d, dtype):
+    # 320 and 448 (five and seven key tiles) once exposed a missing barrier
+    # between the first tile's S and the refill of its K stage
     announce(f"ragged N={n} d={d} causal={causal} {dtype}")
     inputs = random_inputs(2, 3, n, d, dtype, seed=7000 + n + d)
     check_forward_full(inputs, causal, 1.0 / math.sqrt(d))

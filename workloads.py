@@ -105,3 +105,28 @@ def random_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int,
     """Ad-hoc seeded N(0,1)*mult inputs for edge-case shapes (ragged N etc.)."""
     p = Problem("adhoc", B, H, N, d, dtype, False, seed, backward=with_do, qkv_mult=mult)
     return make_inputs(p)
+
+
+def block_mask(heads: int, n: int, block_q: int, block_k: int, kind: str, seed: int,
+               density: float = 0.5, window: int = 2):
+    """Seeded uint8 block masks [heads, ceil(n/block_q), ceil(n/block_k)] (an input, no attention arithmetic).
+
+    kind: "random" (each block kept with probability `density`), "ones",
+    "local" (key blocks whose start lies within `window` query-block widths of
+    the row block, sliding-window attention) or "local_global" (local plus the
+    first key block column, as in long-document patterns).
+    """
+    tq, tk = -(-n // block_q), -(-n // block_k)
+    g = torch.Generator().manual_seed(seed)
+    if kind == "random":
+        return (torch.rand((heads, tq, tk), generator=g) < density).to(torch.uint8)
+    if kind == "ones":
+        return torch.ones((heads, tq, tk), dtype=torch.uint8)
+    rows = torch.arange(tq)[:, None] * block_q
+    cols = torch.arange(tk)[None, :] * block_k
+    m = (cols <= rows + block_q - 1) & (cols + block_k - 1 >= rows - window * block_q)
+    if kind == "local_global":
+        m[:, 0] = True
+    elif kind != "local":
+        raise ValueError(kind)
+    return m.to(torch.uint8)[None].repeat(heads, 1, 1)
