@@ -169,6 +169,70 @@ def kernel_table(p, avg):
     return out
 
 
+def kept_pairs(mask, n, bq, bk, causal):
+    """Number of (query, key) pairs a block mask keeps, per mask head (exact count)."""
+    import numpy as np
+    m = mask.cpu().numpy() != 0
+    rows = np.arange(n)
+    cols = np.arange(n)
+    out = []
+    for h in range(m.shape[0]):
+        keep = m[h][rows[:, None] // bq, cols[None, :] // bk]
+        if causal:
+            keep &= cols[None, :] <= rows[:, None]
+        out.append(int(keep.sum()))
+    return out
+
+
+def sparse_measurement(fa, torch, dev, steps):
+    """Block-sparse forward on the 16K causal d=128 shape with a sliding-window
+    plus global-column mask; FLOPs counted on the kept (query, key) pairs
+    only, and the dense causal forward on the same inputs for comparison."""
+    from workloads import PROBLEMS, block_mask, make_inputs
+    p = PROBLEMS["causal_16k_d128"]
+    bq = bk = 128
+    window = 8                       # key blocks before the diagonal (1024 keys)
+    mask = block_mask(1, p.N, bq, bk, "local_global", seed=0, window=window).to(dev)
+    inputs = make_inputs(p)
+    q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((p.B, p.H, p.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    raw = fa.load_library()
+
+    def run_sparse():
+        st = raw.fa_forward_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                         mask.data_ptr(), 1, bq, bk, p.B, p.H, p.N, p.d, 1, p.scale, 1, stream)
+        assert st == 0, st
+
+    def run_dense():
+        st = raw.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            p.B, p.H, p.N, p.d, 1, p.scale, 1, stream)
+        assert st == 0, st
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_s, ms_d = timed(run_sparse), timed(run_dense)
+    pairs = kept_pairs(mask, p.N, bq, bk, True)[0] * p.B * p.H
+    dense_pairs = p.N * (p.N + 1) // 2 * p.B * p.H
+    flops = 4.0 * p.d * pairs
+    return {"workload": "causal_16k_d128 with a block mask: 128x128 blocks, sliding window of "
+                        f"{window} key blocks plus the first key block column",
+            "kept_fraction_of_causal_pairs": pairs / dense_pairs, "ms": ms_s, "dense_causal_ms": ms_d,
+            "tflops_on_kept_pairs": flops / ms_s * 1e-9, "frac_peak": flops / ms_s * 1e-9 / PEAK_BF16_TFLOPS,
+            "speedup_vs_dense_causal": ms_d / ms_s}
+
+
 def cpu_baseline(inputs, p, heads):
     """The fp64 oracle on a bounded sample: `heads` whole heads of the workload.
 
@@ -207,7 +271,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="causal_16k_d128_bwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=4, help="whole heads timed on the CPU oracle")
-    ap.add_argument("--no-extra", action="store_true", help="skip the N=4K, d=128 side measurement")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the side measurements (N=4K d=128 fwd+bwd, block-sparse 16K forward)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM counters)")
     args = ap.parse_args(argv)
@@ -264,6 +329,8 @@ def main(argv=None):
                           "fwd_tflops": k4["fwd"]["tflops"], "fwd_frac_peak": k4["fwd"]["frac_peak"],
                           "bwd_tflops": k4["bwd_total"]["tflops"], "bwd_frac_peak": k4["bwd_total"]["frac_peak"]}
         del s4
+        torch.cuda.empty_cache()
+        extra["block_sparse_16k_d128"] = sparse_measurement(fa, torch, dev, max(5, args.steps // 2))
         torch.cuda.empty_cache()
 
     out = {
