@@ -35,6 +35,10 @@ Sources (page title -> part used):
   Flashattention*: attention under a mask M in {0,1}^{N x N} whose nonzero
   entries come in blocks of a coarser block mask, computed by skipping the
   zero blocks.
+* "Как работает FlashAttention математически", section 9 (FlashDecoding:
+  generation with cached K, V and a single new query token) with the merge
+  of partial results over key blocks from "Overview of Flash Attention
+  series", section *Tiling* (m = max(m1, m2), l = e^(m1-m) l1 + e^(m2-m) l2).
 
 Readings taken where the pages are silent or disagree (each one is listed in
 the design notes of the repository):
@@ -48,6 +52,9 @@ the design notes of the repository):
   the unmasked j, natural log, of the *scaled* scores.
 * In the coreui worked example the split is along keys (what the primer calls
   T_c / B_c); a block holds keys [j*Bc, (j+1)*Bc), end exclusive.
+* Decoding: the Nq query rows are the last Nq positions of the sequence, so
+  with the causal mask query i sees keys 0 .. Nk - Nq + i (the rows line up
+  with the end of the key sequence); without it, every key.
 * Block-sparse attention: the page writes softmax(S o 1_M) with masked
   entries set to 0, but its algorithm skips the zero blocks, so they carry no
   weight at all.  Reading: masked entries are excluded (-inf), as for the
@@ -82,6 +89,10 @@ __all__ = [
     "expand_block_mask",
     "forward_block_sparse_head",
     "forward_block_sparse",
+    "decode_head",
+    "decode",
+    "merge_partials",
+    "split_kv_decode_head",
 ]
 
 
@@ -452,3 +463,84 @@ def forward_block_sparse(q, k, v, block_mask, block_q: int, block_k: int, causal
             o[b, h], lse[b, h] = forward_block_sparse_head(q[b, h], k[b, h], v[b, h], bm[h if bm.shape[0] > 1 else 0],
                                                            block_q, block_k, causal, scale)
     return o, lse
+
+
+def decode_head(q, k, v, causal: bool = False, scale: Optional[float] = None):
+    """Attention of Nq new query rows over Nk cached keys, one head: (O, lse).
+
+    The queries are the last Nq positions of the sequence: with ``causal``,
+    query i sees keys 0 .. Nk - Nq + i; without it, all Nk keys
+    ("Как работает FlashAttention математически", section 9, FlashDecoding:
+    K, V cached, Q the new token(s)).  q: [Nq, d]; k, v: [Nk, d].
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    nq, nk = q.shape[0], k.shape[0]
+    s = scale * (q @ k.T)
+    if causal:
+        rows = np.arange(nq)[:, None] + (nk - nq)
+        cols = np.arange(nk)[None, :]
+        s = np.where(cols > rows, -np.inf, s)
+    p, m, l = softmax_stats(s)
+    return p @ v, m + np.log(l)
+
+
+def decode(q, k, v, causal: bool = False, scale: Optional[float] = None):
+    """:func:`decode_head` over [B, H, Nq, d] queries and [B, H, Nk, d] keys/values."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    o = np.empty(q.shape[:-1] + (v.shape[-1],))
+    lse = np.empty(q.shape[:-1])
+    for idx in np.ndindex(*q.shape[:-2]):
+        o[idx], lse[idx] = decode_head(q[idx], k[idx], v[idx], causal, scale)
+    return o, lse
+
+
+def merge_partials(o_parts, lse_parts):
+    """Merge attention results over disjoint key blocks into one.
+
+    Each part s holds O_s = softmax over its keys times V and lse_s = ln of
+    its normaliser.  With lse = ln sum_s e^(lse_s), the whole-row result is
+    O = sum_s e^(lse_s - lse) O_s ("Overview of Flash Attention series",
+    Tiling: the two-block decomposition of m and l, written with lse = m +
+    ln l).  A part whose keys were all masked has lse_s = -inf and weight 0.
+    o_parts: [S, Nq, d]; lse_parts: [S, Nq].
+    """
+    o_parts, lse_parts = _as_f64(o_parts), _as_f64(lse_parts)
+    m = np.max(lse_parts, axis=0)
+    w = np.exp(lse_parts - m[None, :])
+    tot = np.sum(w, axis=0)
+    lse = m + np.log(tot)
+    o = np.sum(w[:, :, None] * o_parts, axis=0) / tot[:, None]
+    return o, lse
+
+
+def split_kv_decode_head(q, k, v, splits: int, causal: bool = False, scale: Optional[float] = None):
+    """Split-KV decoding by the algorithm's steps: cut the Nk keys into
+    ``splits`` consecutive chunks, attend to each chunk alone (partial O and
+    lse per chunk; queries with no visible key in a chunk get lse = -inf),
+    then merge the partials with :func:`merge_partials`."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    nq, nk = q.shape[0], k.shape[0]
+    bounds = np.linspace(0, nk, splits + 1).round().astype(int)
+    o_parts, lse_parts = [], []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        s = scale * (q @ k[a:b].T)
+        if causal:
+            rows = np.arange(nq)[:, None] + (nk - nq)
+            cols = np.arange(a, b)[None, :]
+            s = np.where(cols > rows, -np.inf, s)
+        o_s = np.zeros((nq, v.shape[1]))
+        lse_s = np.full(nq, -np.inf)
+        live = ~np.all(np.isneginf(s), axis=1) if s.shape[1] else np.zeros(nq, dtype=bool)
+        if np.any(live):
+            p, m, l = softmax_stats(s[live])
+            o_s[live] = p @ v[a:b]
+            lse_s[live] = m + np.log(l)
+        o_parts.append(o_s)
+        lse_parts.append(lse_s)
+    return merge_partials(np.stack(o_parts), np.stack(lse_parts))

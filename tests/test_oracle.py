@@ -455,3 +455,82 @@ def test_block_sparse_pins_catch_planted_mistakes():
     assert not np.allclose(o_tr, o_b, atol=1e-6)
     o_ok, _ = ref.forward_block_sparse_head(q, k, v, bm, blk, blk, False, 0.7)
     np.testing.assert_allclose(o_ok, o_b, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- decoding (split-KV)
+# "Как работает FlashAttention математически" section 9 (FlashDecoding) and the
+# merge of key-block partials from "Overview of Flash Attention series", Tiling.
+
+@pytest.mark.parametrize("nq,nk", [(1, 17), (3, 40), (8, 8), (5, 64)])
+def test_decode_is_the_last_rows_of_causal_attention(nq, nk):
+    """The Nq new queries are the last rows of a length-Nk causal problem."""
+    d = 6
+    q_full, k, v = (_rand((nk, d), 800 + i + nq) for i in range(3))
+    o_full, lse_full = ref.forward_head(q_full, k, v, True, 0.45)
+    o, lse = ref.decode_head(q_full[nk - nq:], k, v, True, 0.45)
+    np.testing.assert_allclose(o, o_full[nk - nq:], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_full[nk - nq:], rtol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_matches_torch_sdpa_float64(causal):
+    nq, nk, d = 4, 37, 16
+    q, k, v = _rand((2, 3, nq, d), 810), _rand((2, 3, nk, d), 811), _rand((2, 3, nk, d), 812)
+    o, lse = ref.decode(q, k, v, causal, 0.3)
+    mask = None
+    if causal:
+        mask = torch.from_numpy(np.arange(nk)[None, :] <= np.arange(nq)[:, None] + nk - nq)
+    o_t = torch.nn.functional.scaled_dot_product_attention(*(torch.from_numpy(x) for x in (q, k, v)),
+                                                           attn_mask=mask, scale=0.3)
+    np.testing.assert_allclose(o, o_t.numpy(), rtol=1e-12, atol=1e-13)
+    s = 0.3 * np.einsum("bhid,bhjd->bhij", q, k)
+    if causal:
+        s = np.where(mask.numpy(), s, -np.inf)
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(s, axis=-1), rtol=1e-12)
+
+
+def test_decode_single_query_brute_force():
+    nk, d = 11, 3
+    q, k, v = _rand((1, d), 820), _rand((nk, d), 821), _rand((nk, d), 822)
+    o, lse = ref.decode_head(q, k, v, False, 0.9)
+    s = [0.9 * math.fsum(q[0, c] * k[j, c] for c in range(d)) for j in range(nk)]
+    mx = max(s)
+    w = [math.exp(x - mx) for x in s]
+    tot = math.fsum(w)
+    np.testing.assert_allclose(o[0], [math.fsum(w[j] * v[j, c] for j in range(nk)) / tot for c in range(d)],
+                               rtol=1e-13, atol=1e-15)
+    assert abs(lse[0] - (mx + math.log(tot))) < 1e-13
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_kv_equals_definition(splits, causal):
+    nq, nk, d = 5, 50, 8
+    q, k, v = _rand((nq, d), 830), _rand((nk, d), 831, 2.0), _rand((nk, d), 832)
+    o, lse = ref.split_kv_decode_head(q, k, v, splits, causal, 0.6)
+    o_d, lse_d = ref.decode_head(q, k, v, causal, 0.6)
+    np.testing.assert_allclose(o, o_d, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_d, rtol=1e-12)
+
+
+def test_merge_of_two_blocks_is_the_tiling_identity():
+    """Two key blocks of the coreui worked example merge to the one-shot result."""
+    s = np.array([1.0, 2.0, 3.0, 10.0])
+    v = np.array([[1.0, 2.0], [3.0, 4.0], [5.0, 6.0], [7.0, 8.0]])
+    parts_o, parts_l = [], []
+    for a in (0, 2):
+        e = np.exp(s[a:a + 2] - s[a:a + 2].max())
+        parts_o.append((e / e.sum()) @ v[a:a + 2])
+        parts_l.append(s[a:a + 2].max() + math.log(e.sum()))
+    o, lse = ref.merge_partials(np.array(parts_o)[:, None, :], np.array(parts_l)[:, None])
+    e = np.exp(s - s.max())
+    np.testing.assert_allclose(o[0], (e / e.sum()) @ v, rtol=1e-14)
+    assert abs(lse[0] - (s.max() + math.log(e.sum()))) < 1e-14
+    # a fully masked part (lse = -inf) carries no weight
+    o2, lse2 = ref.merge_partials(np.array(parts_o + [np.full(2, 9.0)])[:, None, :],
+                                  np.array(parts_l + [-np.inf])[:, None])
+    np.testing.assert_allclose(o2, o, rtol=1e-15)
+    # a wrong sign in the weights is caught
+    m = max(parts_l)
+    bad = sum(math.exp(m - l) * po for l, po in zip(parts_l, parts_o))
+    assert not np.allclose(bad / sum(math.exp(m - l) for l in parts_l), o[0], atol=1e-6)
