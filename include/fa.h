@@ -58,7 +58,7 @@ enum fa_dtype {
 enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,      /* a required pointer is NULL (non-empty problem) */
-  FA_ERR_SHAPE = 2,     /* B, H or N negative, or B*H*N*d overflows */
+  FA_ERR_SHAPE = 2,     /* B, H or N negative, or one head's N*d elements exceed 2^31 - 1 bytes */
   FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 */
   FA_ERR_DTYPE = 4,     /* dtype is not an fa_dtype */
   FA_ERR_SCALE = 5,     /* scale is NaN, infinite or negative */
@@ -103,6 +103,31 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
                             const unsigned char* block_mask, int mask_heads, int block_q, int block_k,
                             int B, int H, int N, int d, int causal, float scale, int dtype, void* stream);
+
+/*
+ * Split-KV decoding ("Как работает FlashAttention математически", section 9,
+ * FlashDecoding): Nq new query rows attend to Nk cached keys and values.
+ *   q, o: [B, H, Nq, d] with 1 <= Nq <= 32 (Nq = 0 is an empty problem);
+ *   k, v: [B, H, Nk, d] with Nk >= 1 (the cache);  lse: [B, H, Nq] float32.
+ *   The queries are the LAST Nq positions of the sequence: causal != 0 lets
+ *   query i see keys 0 .. Nk - Nq + i (and requires Nq <= Nk); causal = 0
+ *   lets every query see all Nk keys.
+ * The keys of each head are cut into num_splits consecutive chunks (0 picks
+ * a number that fills the GPU; more chunks than 32-key tiles are not used).
+ * Each chunk's partial result is written to `workspace`, and a second kernel
+ * merges them with the rule for concatenated key blocks ("Overview of Flash
+ * Attention series", Tiling).  `workspace` is a device buffer of at least
+ * fa_decode_workspace_size(B, H, Nq, Nk, d, num_splits) bytes, 256-byte
+ * aligned; contents on entry are ignored, on exit unspecified.  Shape errors
+ * (Nq > 32, Nk < 1, causal with Nq > Nk, num_splits < 0) return FA_ERR_SHAPE.
+ * Everything else as fa_forward.
+ */
+size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits);
+/* The number of key chunks fa_decode uses for these sizes (0 for invalid sizes). */
+int fa_decode_num_splits(int B, int H, int Nk, int num_splits);
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Nq, int Nk, int d, int causal, float scale, int dtype,
+              int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace that fa_backward needs: two fp32 row statistics

@@ -17,12 +17,13 @@ from typing import Optional, Tuple
 
 from . import _lib
 from ._lib import (FA_BF16, FA_F32, FaError, fa_backward, fa_backward_dkdv, fa_backward_dq,
-                   fa_backward_preprocess, fa_backward_workspace_size, fa_forward, fa_forward_block_sparse,
-                   fa_strerror)
+                   fa_backward_preprocess, fa_backward_workspace_size, fa_decode, fa_decode_num_splits,
+                   fa_decode_workspace_size, fa_forward, fa_forward_block_sparse, fa_strerror)
 
-__all__ = ["forward", "forward_block_sparse", "backward", "workspace_size", "FaError", "FA_F32", "FA_BF16",
-           "fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_size",
-           "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_strerror", "load_library",
+__all__ = ["forward", "forward_block_sparse", "backward", "decode", "workspace_size", "FaError", "FA_F32",
+           "FA_BF16", "fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_size",
+           "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_decode",
+           "fa_decode_workspace_size", "fa_decode_num_splits", "fa_strerror", "load_library",
            "backward_stages"]
 
 
@@ -118,6 +119,44 @@ def forward_block_sparse(q, k, v, block_mask, block_q: int, block_k: int, causal
                                  scale, _dtype_code(q), _stream_ptr(q.device))
     if st != 0:
         raise FaError(st, "fa_forward_block_sparse")
+    return out, lse
+
+
+def decode(q, k, v, causal: bool = True, scale: Optional[float] = None, num_splits: int = 0,
+           out=None, lse=None, workspace=None):
+    """Split-KV decoding: Nq <= 32 new queries against a cache of Nk keys/values.
+
+    q: [B, H, Nq, d]; k, v: [B, H, Nk, d] (same dtype and device).  The
+    queries are the last Nq positions: with ``causal`` query i sees keys
+    0 .. Nk - Nq + i, otherwise all Nk.  ``num_splits`` = 0 lets the library
+    choose how many key chunks each head is cut into.
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if q.device.type != "cuda":
+        raise ValueError("tensors must live on a ROCm device")
+    _check("q", q, q.shape, q.dtype, q.device)
+    for name, t in (("k", k), ("v", v)):
+        _check(name, t, (B, H, Nk, d), q.dtype, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check("out", out, q.shape, q.dtype, q.device)
+    _check("lse", lse, (B, H, Nq), torch.float32, q.device)
+    need = fa_decode_workspace_size(B, H, Nq, Nk, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
+                   causal, scale, _dtype_code(q), num_splits, workspace.data_ptr(), workspace.numel(),
+                   _stream_ptr(q.device))
+    if st != 0:
+        raise FaError(st, "fa_decode")
     return out, lse
 
 

@@ -21,7 +21,8 @@ STATUS = {
     5: "FA_ERR_SCALE", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ALIGN", 9: "FA_ERR_MASK",
 }
 EXPORTED = ("fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_size",
-            "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_strerror")
+            "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_decode",
+            "fa_decode_workspace_size", "fa_decode_num_splits", "fa_strerror")
 
 _lock = threading.Lock()
 _lib = None
@@ -61,6 +62,12 @@ def load() -> ctypes.CDLL:
         lib.fa_backward_dkdv.restype = i
         lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
         lib.fa_backward_dq.restype = i
+        lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+        lib.fa_decode.restype = i
+        lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i]
+        lib.fa_decode_workspace_size.restype = sz
+        lib.fa_decode_num_splits.argtypes = [i, i, i, i]
+        lib.fa_decode_num_splits.restype = i
         lib.fa_strerror.argtypes = [i]
         lib.fa_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -101,6 +108,20 @@ def fa_backward_dq(q, k, v, dout, dq, B, H, N, d, causal, scale, dtype,
 
 def fa_backward_workspace_size(B, H, N, d) -> int:
     return load().fa_backward_workspace_size(B, H, N, d)
+
+
+def fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, num_splits,
+              workspace, workspace_bytes, stream) -> int:
+    return load().fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal), float(scale), dtype,
+                            num_splits, workspace, workspace_bytes, stream)
+
+
+def fa_decode_workspace_size(B, H, Nq, Nk, d, num_splits) -> int:
+    return load().fa_decode_workspace_size(B, H, Nq, Nk, d, num_splits)
+
+
+def fa_decode_num_splits(B, H, Nk, num_splits) -> int:
+    return load().fa_decode_num_splits(B, H, Nk, num_splits)
 
 
 def fa_strerror(status: int) -> str:

@@ -19,11 +19,12 @@ int check_shape(int B, int H, int N, int d, int dtype, float scale, bool* empty)
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
-  // B*H*N*d elements and B*H*N rows must fit the kernels' index arithmetic:
-  // rows and per-head offsets use 32-bit ints, whole-tensor offsets 64-bit.
+  // Sizes must fit the kernels' index arithmetic: rows and per-head byte
+  // offsets use 32-bit ints, whole-tensor offsets 64-bit.
   const int64_t rows = (int64_t)B * H * N;
   const int64_t tiles = ((int64_t)N + 127) / 128 * B * H;   // workgroups of the largest grid
-  if ((int64_t)B * H > INT32_MAX || (int64_t)N * d > INT32_MAX || tiles > INT32_MAX ||
+  const int64_t head_bytes = (int64_t)N * d * (dtype == FA_BF16 ? 2 : 4);
+  if ((int64_t)B * H > INT32_MAX || head_bytes > INT32_MAX || tiles > INT32_MAX ||
       rows > ((int64_t)1 << 40))
     return FA_ERR_SHAPE;
   *empty = rows == 0;
@@ -102,6 +103,58 @@ int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
   fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal ? 1 : 0, dtype, scale, block_mask, mask_heads, block_q, block_k};
   return hip_status(fa::launch_forward(a, static_cast<hipStream_t>(stream)));
+}
+
+// Decode shapes: Nq in [0, 32], Nk >= 1 unless the problem is empty, causal needs Nq <= Nk.
+static int check_decode(int B, int H, int Nq, int Nk, int d, int causal, int dtype, float scale, bool* empty) {
+  bool e1 = false, e2 = false;
+  int st = check_shape(B, H, Nq, d, dtype, scale, &e1);
+  if (st != FA_OK) return st;
+  st = check_shape(B, H, Nk, d, dtype, scale, &e2);
+  if (st != FA_OK) return st;
+  if (Nq > fa::kDecodeMaxNq) return FA_ERR_SHAPE;
+  *empty = e1;
+  if (e1) return FA_OK;
+  if (Nk < 1 || (causal && Nq > Nk)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+static size_t decode_ws_bytes(int B, int H, int Nq, int d, int splits) {
+  const size_t rows = (size_t)B * H * splits * Nq;
+  return fa::align256(rows * d * sizeof(float)) + fa::align256(rows * sizeof(float));
+}
+
+size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits) {
+  bool empty = false;
+  if (num_splits < 0 || check_decode(B, H, Nq, Nk, d, 0, FA_BF16, 1.f, &empty) != FA_OK || empty) return 0;
+  return decode_ws_bytes(B, H, Nq, d, fa::decode_splits(B, H, Nk, num_splits));
+}
+
+int fa_decode_num_splits(int B, int H, int Nk, int num_splits) {
+  if (B <= 0 || H <= 0 || Nk <= 0 || num_splits < 0) return 0;
+  return fa::decode_splits(B, H, Nk, num_splits);
+}
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
+              int causal, float scale, int dtype, int num_splits, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  bool empty = false;
+  const int st = check_decode(B, H, Nq, Nk, d, causal, dtype, scale, &empty);
+  if (st != FA_OK) return st;
+  if (num_splits < 0) return FA_ERR_SHAPE;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  const int splits = fa::decode_splits(B, H, Nk, num_splits);
+  if ((int64_t)B * H * splits > INT32_MAX) return FA_ERR_SHAPE;
+  const size_t need = decode_ws_bytes(B, H, Nq, d, splits);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  const size_t rows = (size_t)B * H * splits * Nq;
+  fa::DecArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, causal ? 1 : 0, dtype, splits, scale,
+                reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + fa::align256(rows * d * sizeof(float)))};
+  return hip_status(fa::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {

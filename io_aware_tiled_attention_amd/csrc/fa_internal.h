@@ -40,12 +40,44 @@ struct BwdArgs {
   float* nlse;     // [B*H*N]   -lse_i, exponent domain   (workspace)
 };
 
+struct DecArgs {
+  const void* q;     // [B, H, Nq, d]
+  const void* k;     // [B, H, Nk, d]
+  const void* v;
+  void* o;           // [B, H, Nq, d]
+  float* lse;        // [B, H, Nq]
+  int B, H, Nq, Nk, d, causal, dtype, splits;
+  float scale;
+  float* opart;      // [B*H][splits][Nq][d]   partial outputs  (workspace)
+  float* lpart;      // [B*H][splits][Nq]      partial lse      (workspace)
+};
+
+constexpr int kDecodeMaxNq = 32;      // query rows per decode call (one matrix-core tile)
+constexpr int kDecodeTile = 32;       // keys per decode tile
+
+// Number of key chunks of a decode call: `requested` if positive, else enough
+// (head, chunk) workgroups to cover the GPU several times over, with at
+// least 8 tiles (256 keys) per chunk; never more chunks than tiles.
+inline int decode_splits(int B, int H, int Nk, int requested) {
+  const long long tiles = ((long long)Nk + kDecodeTile - 1) / kDecodeTile;
+  long long s = requested;
+  if (s <= 0) {
+    const long long bh = (long long)B * H;
+    s = (2048 + bh - 1) / bh;
+    const long long cap = tiles / 8 > 1 ? tiles / 8 : 1;
+    if (s > cap) s = cap;
+  }
+  if (s > tiles) s = tiles;
+  return s < 1 ? 1 : (int)s;
+}
+
 // Workspace carve-up shared by fa_backward_workspace_size and fa_backward.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline size_t ws_dsum_bytes(size_t rows) { return align256(rows * sizeof(float)); }
 inline size_t ws_bytes(size_t rows) { return 2 * ws_dsum_bytes(rows); }
 
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecArgs& a, hipStream_t stream);
 // backward stages (bit mask; 7 = all): D, then dK/dV, then dQ
 constexpr int kStagePre = 1, kStageDkDv = 2, kStageDq = 4;
 hipError_t launch_backward(const BwdArgs& a, int stages, hipStream_t stream);

@@ -178,3 +178,66 @@ def test_block_sparse_accepts_per_head_masks_and_large_blocks_in_validation():
     # NULL pointer check that follows geometry)
     assert fwd_sparse(mask_heads=2, block_q=256, block_k=128, q=0) == 1
     assert fwd_sparse(N=65536, block_q=32, block_k=64, k=0) == 1
+
+
+def test_per_head_byte_size_limit():
+    # one head of fp32 d=128 at N = 2^22 spans 2^31 bytes: past the 32-bit offsets
+    assert fwd(N=1 << 22, d=128, dtype=_lib.FA_F32) == 2
+    # the same N in bf16 spans 2^30 bytes: validation passes, the NULL check fails next
+    assert fwd(N=1 << 22, d=128, dtype=_lib.FA_BF16, q=0) == 1
+
+
+def dec(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, H=4, Nq=1, Nk=4096, d=128, causal=1, scale=0.125,
+             dtype=_lib.FA_BF16, splits=0, ws=0x100000, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return fa.fa_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                        a["causal"], a["scale"], a["dtype"], a["splits"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
+    (dict(Nq=33), 2), (dict(Nq=-1), 2), (dict(Nk=0), 2), (dict(Nk=-4), 2), (dict(Nq=8, Nk=7), 2),
+    (dict(splits=-1), 2), (dict(B=-1), 2),
+    (dict(d=96), 3), (dict(dtype=5), 4), (dict(scale=float("inf")), 5),
+    (dict(ws=0), 6), (dict(ws_bytes=64), 6),
+    (dict(ws=0x100080), 8), (dict(k=FAKE + 2), 8), (dict(lse=FAKE + 4), 8),
+])
+def test_decode_rejects_invalid_arguments(kw, status):
+    assert dec(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [
+    dict(Nq=8, Nk=7, causal=0, q=0),     # non-causal: Nq > Nk is a valid shape
+    dict(Nq=32, Nk=32, q=0),
+])
+def test_decode_valid_shapes_pass_validation(kw):
+    assert dec(**kw) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(Nq=0), dict(B=0), dict(H=0), dict(Nq=0, Nk=0, q=0, k=0, ws=0)])
+def test_decode_empty_problem_is_a_noop(kw):
+    assert dec(**kw) == 0
+
+
+def test_decode_split_count_and_workspace_size():
+    # automatic: enough (head, chunk) workgroups for the GPU, >= 8 tiles of 32 keys per chunk
+    assert fa.fa_decode_num_splits(1, 32, 65536, 0) == 64
+    assert fa.fa_decode_num_splits(8, 32, 8192, 0) == 8
+    assert fa.fa_decode_num_splits(64, 32, 8192, 0) == 1
+    assert fa.fa_decode_num_splits(1, 1, 300, 0) == 1
+    assert fa.fa_decode_num_splits(1, 1, 4096, 0) == 16
+    # requested: kept, but never more chunks than 32-key tiles
+    assert fa.fa_decode_num_splits(1, 1, 4096, 7) == 7
+    assert fa.fa_decode_num_splits(1, 1, 65, 100) == 3
+    assert fa.fa_decode_num_splits(1, 1, 65, -1) == 0
+    for B, H, nq, nk, d, s in [(1, 32, 1, 65536, 128, 0), (2, 3, 5, 1000, 64, 4), (1, 1, 32, 1, 128, 0)]:
+        S = fa.fa_decode_num_splits(B, H, nk, s)
+        rows = B * H * S * nq
+        want = -(-rows * d * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+        assert fa.fa_decode_workspace_size(B, H, nq, nk, d, s) == want
+    assert dec(Nq=5, Nk=1000, d=64, B=2, H=3, splits=4, ws_bytes=fa.fa_decode_workspace_size(2, 3, 5, 1000, 64, 4) - 1) == 6
+    assert dec(Nq=5, Nk=1000, d=64, B=2, H=3, splits=4, ws_bytes=fa.fa_decode_workspace_size(2, 3, 5, 1000, 64, 4),
+               q=0) == 1
+    assert fa.fa_decode_workspace_size(1, 1, 33, 64, 128, 0) == 0
+    assert fa.fa_decode_workspace_size(1, 1, 0, 64, 128, 0) == 0

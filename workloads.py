@@ -130,3 +130,15 @@ def block_mask(heads: int, n: int, block_q: int, block_k: int, kind: str, seed: 
     elif kind != "local":
         raise ValueError(kind)
     return m.to(torch.uint8)[None].repeat(heads, 1, 1)
+
+
+def decode_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, seed: int, mult: float = 1.0):
+    """Seeded N(0,1)*mult decoding inputs: q [B, H, Nq, d] (the newest Nq
+    positions) and a cache k, v [B, H, Nk, d]; a dict of CPU tensors."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    q = torch.randn((B, H, Nq, d), generator=g, dtype=torch.float32) * mult
+    k = torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32) * mult
+    v = torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32) * mult
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    return {name: t.to(td).contiguous() for name, t in (("q", q), ("k", k), ("v", v))}
