@@ -12,7 +12,7 @@ FLOP counting convention: forward 4*B*H*N^2*d, halved when causal; backward
 the wall time of a step, in TFLOP/s.
 
 Prints ONE JSON line.  Options: --gpus N (only 1: the path runs on one GPU),
---steps K, --warmup W, --no-cpu-baseline, --no-extra.
+--steps K, --warmup W, --no-cpu-baseline, --no-extra, --decode-only.
 """
 from __future__ import annotations
 
@@ -233,6 +233,54 @@ def sparse_measurement(fa, torch, dev, steps):
             "speedup_vs_dense_causal": ms_d / ms_s}
 
 
+DECODE_SHAPES = [(1, 32, 1, 65536), (8, 32, 1, 8192)]    # (B, H, Nq, Nk), d = 128, bf16, causal
+
+
+def decode_measurement(fa, torch, dev, steps, shapes=None):
+    """Split-KV decoding (fa_decode, partial + merge kernels) on long caches.
+    The work is bound by HBM: the algorithmic bytes are one read of K and V
+    plus Q, and the writes of O and lse (the partial results in the workspace
+    are the method's own overhead and not counted); GB/s against 8 TB/s."""
+    from workloads import decode_inputs
+    raw = fa.load_library()
+    stream = torch.cuda.current_stream().cuda_stream
+    out = []
+    d = 128
+    for B, H, Nq, Nk in (DECODE_SHAPES if shapes is None else shapes):
+        inp = decode_inputs(B, H, Nq, Nk, d, "bf16", seed=B * 131 + Nk)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        del inp
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+        splits = raw.fa_decode_num_splits(B, H, Nk, 0)
+        ws_bytes = raw.fa_decode_workspace_size(B, H, Nq, Nk, d, 0)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        scale = d ** -0.5
+
+        def run():
+            st = raw.fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Nq,
+                               Nk, d, 1, scale, 1, 0, ws.data_ptr(), ws_bytes, stream)
+            assert st == 0, st
+
+        for _ in range(3):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        kv_bytes = 2 * B * H * Nk * d * 2
+        alg = kv_bytes + 2 * B * H * Nq * d * 2 + B * H * Nq * 4
+        out.append({"B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d, "causal": True, "splits": splits, "ms": ms,
+                    "algorithmic_bytes": alg, "gbs": alg / ms * 1e-6, "frac_hbm_peak": alg / ms * 1e-6 / PEAK_HBM_GBS})
+        del q, k, v, o, lse, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(inputs, p, heads):
     """The fp64 oracle on a bounded sample: `heads` whole heads of the workload.
 
@@ -272,7 +320,12 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=4, help="whole heads timed on the CPU oracle")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the side measurements (N=4K d=128 fwd+bwd, block-sparse 16K forward)")
+                    help="skip the side measurements (N=4K d=128 fwd+bwd, block-sparse 16K forward, "
+                         "split-KV decoding)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the split-KV decoding measurement (one JSON line; for kernel traces)")
+    ap.add_argument("--decode-shape", type=int, default=None,
+                    help="with --decode-only: only this entry of the decoding shapes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM counters)")
     args = ap.parse_args(argv)
@@ -303,6 +356,11 @@ def main(argv=None):
         print(json.dumps({"copy_calibration": {"bytes_read_per_copy": 4 * n, "bytes_written_per_copy": 4 * n,
                                                "copies": 3}}), flush=True)
         return 0
+    if args.decode_only:
+        shapes = None if args.decode_shape is None else [DECODE_SHAPES[args.decode_shape]]
+        print(json.dumps({"decode_bf16_d128": decode_measurement(fa, torch, dev, max(10, args.steps), shapes)}),
+              flush=True)
+        return 0
     p = PROBLEMS[args.workload]
     inputs = make_inputs(p, with_do=True)
     step = Step(fa, torch, inputs, p, dev)
@@ -332,6 +390,7 @@ def main(argv=None):
         torch.cuda.empty_cache()
         extra["block_sparse_16k_d128"] = sparse_measurement(fa, torch, dev, max(5, args.steps // 2))
         torch.cuda.empty_cache()
+        extra["decode_bf16_d128"] = decode_measurement(fa, torch, dev, max(10, args.steps))
 
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -112,15 +112,19 @@ int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o
  *   The queries are the LAST Nq positions of the sequence: causal != 0 lets
  *   query i see keys 0 .. Nk - Nq + i (and requires Nq <= Nk); causal = 0
  *   lets every query see all Nk keys.
- * The keys of each head are cut into num_splits consecutive chunks (0 picks
- * a number that fills the GPU; more chunks than 32-key tiles are not used).
- * Each chunk's partial result is written to `workspace`, and a second kernel
+ * The keys of each head are cut into num_splits chunks of 32-key tiles (0
+ * picks a number that fills the GPU; more chunks than tiles are not used).
+ * Each chunk's partial result goes to `workspace`, and a second kernel
  * merges them with the rule for concatenated key blocks ("Overview of Flash
- * Attention series", Tiling).  `workspace` is a device buffer of at least
- * fa_decode_workspace_size(B, H, Nq, Nk, d, num_splits) bytes, 256-byte
- * aligned; contents on entry are ignored, on exit unspecified.  Shape errors
- * (Nq > 32, Nk < 1, causal with Nq > Nk, num_splits < 0) return FA_ERR_SHAPE.
- * Everything else as fa_forward.
+ * Attention series", Tiling); with one chunk per head the outputs are
+ * written directly.
+ * `workspace`: a device buffer of at least
+ * fa_decode_workspace_size(B, H, Nq, Nk, d, num_splits) bytes (0 bytes, and
+ * NULL allowed, when one chunk per head is used), 256-byte aligned; contents
+ * on entry are ignored, on exit unspecified.  Calls that run concurrently
+ * must not share a workspace.
+ * Shape errors (Nq > 32, Nk < 1, causal with Nq > Nk, num_splits < 0)
+ * return FA_ERR_SHAPE.  Everything else as fa_forward.
  */
 size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits);
 /* The number of key chunks fa_decode uses for these sizes (0 for invalid sizes). */

@@ -129,7 +129,8 @@ def decode(q, k, v, causal: bool = True, scale: Optional[float] = None, num_spli
     q: [B, H, Nq, d]; k, v: [B, H, Nk, d] (same dtype and device).  The
     queries are the last Nq positions: with ``causal`` query i sees keys
     0 .. Nk - Nq + i, otherwise all Nk.  ``num_splits`` = 0 lets the library
-    choose how many key chunks each head is cut into.
+    choose how many key chunks each head is cut into.  ``workspace``: an
+    optional uint8 scratch buffer of at least fa_decode_workspace_size bytes.
     """
     import torch
     if q.dim() != 4 or k.dim() != 4:

@@ -119,7 +119,11 @@ static int check_decode(int B, int H, int Nq, int Nk, int d, int causal, int dty
   return FA_OK;
 }
 
+// Decode workspace: partial O [B*H*S*Nq][d] fp32, then partial lse
+// [B*H*S*Nq] fp32, each region 256-byte aligned.  One chunk per head (S = 1)
+// writes the outputs directly and needs none.
 static size_t decode_ws_bytes(int B, int H, int Nq, int d, int splits) {
+  if (splits == 1) return 0;
   const size_t rows = (size_t)B * H * splits * Nq;
   return fa::align256(rows * d * sizeof(float)) + fa::align256(rows * sizeof(float));
 }
@@ -148,12 +152,16 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
   const int splits = fa::decode_splits(B, H, Nk, num_splits);
   if ((int64_t)B * H * splits > INT32_MAX) return FA_ERR_SHAPE;
   const size_t need = decode_ws_bytes(B, H, Nq, d, splits);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_ALIGN;
-  char* ws = static_cast<char*>(workspace);
-  const size_t rows = (size_t)B * H * splits * Nq;
-  fa::DecArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, causal ? 1 : 0, dtype, splits, scale,
-                reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + fa::align256(rows * d * sizeof(float)))};
+  fa::DecArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, causal ? 1 : 0, dtype, splits, scale, nullptr, nullptr};
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_ALIGN;
+    char* ws = static_cast<char*>(workspace);
+    const size_t rows = (size_t)B * H * splits * Nq;
+    const size_t o_bytes = fa::align256(rows * d * sizeof(float));
+    a.opart = reinterpret_cast<float*>(ws);
+    a.lpart = reinterpret_cast<float*>(ws + o_bytes);
+  }
   return hip_status(fa::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 

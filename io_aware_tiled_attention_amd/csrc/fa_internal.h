@@ -48,22 +48,24 @@ struct DecArgs {
   float* lse;        // [B, H, Nq]
   int B, H, Nq, Nk, d, causal, dtype, splits;
   float scale;
-  float* opart;      // [B*H][splits][Nq][d]   partial outputs  (workspace)
-  float* lpart;      // [B*H][splits][Nq]      partial lse      (workspace)
+  float* opart;      // [B*H][splits][Nq][d]   partial outputs  (workspace; splits > 1)
+  float* lpart;      // [B*H][splits][Nq]      partial lse      (workspace; splits > 1)
 };
 
 constexpr int kDecodeMaxNq = 32;      // query rows per decode call (one matrix-core tile)
 constexpr int kDecodeTile = 32;       // keys per decode tile
 
-// Number of key chunks of a decode call: `requested` if positive, else enough
-// (head, chunk) workgroups to cover the GPU several times over, with at
-// least 8 tiles (256 keys) per chunk; never more chunks than tiles.
+// Number of key chunks of a decode call: `requested` if positive, else about
+// 512 (head, chunk) workgroups -- two per CU, where the measured read rate
+// of the long-cache shapes peaks (more concurrent streams read HBM more
+// slowly) -- with at least 8 tiles (256 keys) per chunk; never more chunks
+// than tiles.
 inline int decode_splits(int B, int H, int Nk, int requested) {
   const long long tiles = ((long long)Nk + kDecodeTile - 1) / kDecodeTile;
   long long s = requested;
   if (s <= 0) {
     const long long bh = (long long)B * H;
-    s = (2048 + bh - 1) / bh;
+    s = (512 + bh - 1) / bh;
     const long long cap = tiles / 8 > 1 ? tiles / 8 : 1;
     if (s > cap) s = cap;
   }

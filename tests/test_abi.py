@@ -221,23 +221,28 @@ def test_decode_empty_problem_is_a_noop(kw):
 
 
 def test_decode_split_count_and_workspace_size():
-    # automatic: enough (head, chunk) workgroups for the GPU, >= 8 tiles of 32 keys per chunk
-    assert fa.fa_decode_num_splits(1, 32, 65536, 0) == 64
-    assert fa.fa_decode_num_splits(8, 32, 8192, 0) == 8
+    # automatic: about 512 (head, chunk) workgroups, >= 8 tiles of 32 keys per chunk
+    assert fa.fa_decode_num_splits(1, 32, 65536, 0) == 16
+    assert fa.fa_decode_num_splits(8, 32, 8192, 0) == 2
     assert fa.fa_decode_num_splits(64, 32, 8192, 0) == 1
     assert fa.fa_decode_num_splits(1, 1, 300, 0) == 1
     assert fa.fa_decode_num_splits(1, 1, 4096, 0) == 16
+    assert fa.fa_decode_num_splits(1, 1, 1 << 20, 0) == 512
     # requested: kept, but never more chunks than 32-key tiles
     assert fa.fa_decode_num_splits(1, 1, 4096, 7) == 7
     assert fa.fa_decode_num_splits(1, 1, 65, 100) == 3
     assert fa.fa_decode_num_splits(1, 1, 65, -1) == 0
-    for B, H, nq, nk, d, s in [(1, 32, 1, 65536, 128, 0), (2, 3, 5, 1000, 64, 4), (1, 1, 32, 1, 128, 0)]:
+    for B, H, nq, nk, d, s in [(1, 32, 1, 65536, 128, 0), (2, 3, 5, 1000, 64, 4), (1, 1, 32, 1, 128, 0),
+                               (64, 32, 1, 8192, 128, 0)]:
         S = fa.fa_decode_num_splits(B, H, nk, s)
         rows = B * H * S * nq
-        want = -(-rows * d * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+        # partial O and partial lse; nothing with one chunk per head
+        want = 0 if S == 1 else -(-rows * d * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
         assert fa.fa_decode_workspace_size(B, H, nq, nk, d, s) == want
     assert dec(Nq=5, Nk=1000, d=64, B=2, H=3, splits=4, ws_bytes=fa.fa_decode_workspace_size(2, 3, 5, 1000, 64, 4) - 1) == 6
     assert dec(Nq=5, Nk=1000, d=64, B=2, H=3, splits=4, ws_bytes=fa.fa_decode_workspace_size(2, 3, 5, 1000, 64, 4),
                q=0) == 1
+    # one chunk per head needs no workspace: NULL passes validation (then the NULL q fails)
+    assert dec(Nk=64, splits=1, ws=0, ws_bytes=0, q=0) == 1
     assert fa.fa_decode_workspace_size(1, 1, 33, 64, 128, 0) == 0
     assert fa.fa_decode_workspace_size(1, 1, 0, 64, 128, 0) == 0

@@ -24,10 +24,14 @@ def _gpu():
     require_gpu()
 
 
-def run_decode(inputs, causal, scale, splits=0):
+def run_decode(inputs, causal, scale, splits=0, workspace=None):
+    """fa_decode on the GPU; O and lse start as NaN so that a row the kernel
+    never writes fails the comparison."""
     dev = torch.device("cuda", 0)
     q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
-    o, lse = fa.decode(q, k, v, causal=causal, scale=scale, num_splits=splits)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=dev)
+    fa.decode(q, k, v, causal=causal, scale=scale, num_splits=splits, out=o, lse=lse, workspace=workspace)
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu()
 
@@ -57,6 +61,8 @@ def check(inputs, o, lse, causal, scale, heads=None):
     ("f32", 2, 2, 5, 300, 64, False, 3),
     ("f32", 1, 1, 16, 16, 128, True, 0),
     ("f32", 1, 2, 32, 2049, 64, True, 9),
+    ("bf16", 1, 2, 3, 8192, 64, True, 100),    # more than 64 chunks: the merge takes two rounds
+    ("f32", 1, 1, 2, 4200, 128, False, 130),   # three merge rounds, chunks of one or two tiles
 ])
 def test_decode_matches_oracle(dtype, B, H, Nq, Nk, d, causal, splits):
     S = fa.fa_decode_num_splits(B, H, Nk, splits)
@@ -82,6 +88,22 @@ def test_decode_result_independent_of_chunk_count(dtype):
     for o, lse in outs[1:]:
         assert float((o - outs[0][0]).abs().max()) <= 2 * tol
         assert float((lse - outs[0][1]).abs().max()) <= TOL_LSE
+
+
+def test_decode_workspace_contents_do_not_matter():
+    """The workspace is scratch: one buffer filled with garbage (0xff bytes,
+    then whatever the previous call left) serves calls with different chunk
+    counts, each exact."""
+    announce("decode workspace reuse: chunk counts 16, 5, 64, 16 on one garbage-filled workspace")
+    dev = torch.device("cuda", 0)
+    B, H, Nq, Nk, d = 2, 3, 4, 4096, 128
+    inputs = decode_inputs(B, H, Nq, Nk, d, "bf16", seed=1303)
+    need = max(fa.fa_decode_workspace_size(B, H, Nq, Nk, d, s) for s in (16, 5, 64))
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=dev)
+    scale = 1.0 / np.sqrt(d)
+    for s in (16, 5, 64, 16):
+        o, lse = run_decode(inputs, True, scale, s, workspace=ws)
+        check(inputs, o, lse, True, scale)
 
 
 def test_decode_equals_last_rows_of_causal_forward():
