@@ -35,6 +35,13 @@ Sources (page title -> part used):
   Flashattention*: attention under a mask M in {0,1}^{N x N} whose nonzero
   entries come in blocks of a coarser block mask, computed by skipping the
   zero blocks.
+* "Как работает FlashAttention математически", section 5 (the backward
+  recomputes P from the saved statistics, and dropout masks are not kept as
+  N x N arrays) and "Overview of Flash Attention series", Backward Pass
+  (masks are regenerated in the backward from what the forward kept).
+  Dropout here draws its mask from the counter-based generator Philox4x32-10
+  (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2,
+  3", SC 2011), written from that paper's definition.
 * "Как работает FlashAttention математически", section 9 (FlashDecoding:
   generation with cached K, V and a single new query token) with the merge
   of partial results over key blocks from "Overview of Flash Attention
@@ -55,6 +62,15 @@ the design notes of the repository):
 * Decoding: the Nq query rows are the last Nq positions of the sequence, so
   with the causal mask query i sees keys 0 .. Nk - Nq + i (the rows line up
   with the end of the key sequence); without it, every key.
+* Dropout: the pages name no generator and no layout.  Reading: dropout
+  acts on the probabilities after the softmax, O = (P o Z) V / (1 - p), with
+  lse that of the undropped scores; the mask Z is a pure function of (seed,
+  offset, head, query, key), so the backward regenerates it.  The drop
+  probability is quantised to t / 256 (t = round(256 p), 0 <= t <= 255): one
+  random byte per element, dropped when the byte is < t.  Element (i, j) of
+  head bh takes byte 4 (i mod 4) + (j mod 4) (little-endian within the four
+  32-bit words) of Philox4x32-10 at counter (j div 4, i div 4, bh, offset)
+  with the 64-bit seed as key.
 * Block-sparse attention: the page writes softmax(S o 1_M) with masked
   entries set to 0, but its algorithm skips the zero blocks, so they carry no
   weight at all.  Reading: masked entries are excluded (-inf), as for the
@@ -93,6 +109,12 @@ __all__ = [
     "decode",
     "merge_partials",
     "split_kv_decode_head",
+    "philox4x32",
+    "dropout_threshold",
+    "dropout_keep_mask",
+    "forward_dropout_head",
+    "backward_dropout_head",
+    "finite_difference_grads_dropout",
 ]
 
 
@@ -544,3 +566,134 @@ def split_kv_decode_head(q, k, v, splits: int, causal: bool = False, scale: Opti
         o_parts.append(o_s)
         lse_parts.append(lse_s)
     return merge_partials(np.stack(o_parts), np.stack(lse_parts))
+
+
+# --- Dropout with a regenerated mask ---------------------------------------
+
+_M32 = 0xFFFFFFFF
+# Philox4x32 multipliers and Weyl key increments, as published by Salmon et al.
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)
+
+
+def philox4x32(counter, key, rounds: int = 10) -> np.ndarray:
+    """Philox4x32-R of Salmon, Moraes, Dror and Shaw (SC 2011).
+
+    counter: integers [..., 4] (32-bit words), key: [..., 2] (broadcastable).
+    One round maps (c0, c1, c2, c3) with key (k0, k1) to
+      (hi(M1 c2) ^ c1 ^ k0,  lo(M1 c2),  hi(M0 c0) ^ c3 ^ k1,  lo(M0 c0)),
+    hi/lo being the upper/lower 32 bits of the 64-bit product; the key is
+    bumped by the Weyl constants (W0, W1) before every round after the first.
+    Returns the four 32-bit output words as uint64 values [..., 4].
+    """
+    c = np.asarray(counter, dtype=np.uint64) & np.uint64(_M32)
+    k = np.asarray(key, dtype=np.uint64) & np.uint64(_M32)
+    c0, c1, c2, c3 = (c[..., n] for n in range(4))
+    k0, k1 = k[..., 0], k[..., 1]
+    m0, m1 = np.uint64(_PHILOX_M[0]), np.uint64(_PHILOX_M[1])
+    mask, sh = np.uint64(_M32), np.uint64(32)
+    for r in range(rounds):
+        if r > 0:
+            k0 = (k0 + np.uint64(_PHILOX_W[0])) & mask
+            k1 = (k1 + np.uint64(_PHILOX_W[1])) & mask
+        p0 = m0 * c0
+        p1 = m1 * c2
+        c0, c1, c2, c3 = ((p1 >> sh) ^ c1 ^ k0, p1 & mask, (p0 >> sh) ^ c3 ^ k1, p0 & mask)
+    return np.stack([c0, c1, c2, c3], axis=-1)
+
+
+def dropout_threshold(p_drop: float) -> int:
+    """t = round(256 p) in float32 arithmetic (half away from zero): an element is
+    dropped when its random byte is < t, so the drop probability is t / 256."""
+    t = int(math.floor(float(np.float32(np.float32(p_drop) * np.float32(256.0))) + 0.5))
+    if not 0 <= t <= 255:
+        raise ValueError("dropout probability must round to t / 256 with 0 <= t <= 255")
+    return t
+
+
+def dropout_keep_mask(bh: int, n_q: int, n_k: int, seed: int, offset: int, t: int) -> np.ndarray:
+    """Keep mask Z [n_q, n_k] (bool) of head index ``bh`` (= b * H + h).
+
+    Element (i, j) uses byte 4 (i % 4) + (j % 4) of
+    philox4x32(counter=(j // 4, i // 4, bh, offset), key=(seed low, seed high)),
+    bytes numbered little-endian within the four output words; kept when
+    that byte is >= t.
+    """
+    rows = np.arange(n_q)
+    cols = np.arange(n_k)
+    qg = (rows // 4)[:, None]
+    kg = (cols // 4)[None, :]
+    ctr = np.stack(np.broadcast_arrays(kg, qg, np.full_like(qg, bh), np.full_like(qg, offset)), axis=-1)
+    key = np.array([seed & _M32, (seed >> 32) & _M32], dtype=np.uint64)
+    words = philox4x32(ctr, key)                                    # [n_q, n_k, 4]
+    word = np.take_along_axis(words, (rows % 4)[:, None, None].repeat(n_k, axis=1), axis=-1)[..., 0]
+    byte = (word >> (8 * (cols % 4)).astype(np.uint64)[None, :]) & np.uint64(0xFF)
+    return byte >= np.uint64(t)
+
+
+def forward_dropout_head(q, k, v, keep, t: int, causal: bool = False, scale: Optional[float] = None):
+    """Attention with dropout on the probabilities, one head: returns (O, lse).
+
+    P = softmax(S) as in :func:`forward_head`; O = (P o Z) V / (1 - t/256)
+    with the keep mask Z = ``keep``; lse is that of the undropped S.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    s = scores(q, k, scale, causal)
+    p, m, l = softmax_stats(s)
+    rs = 256.0 / (256.0 - t)
+    o = (p * keep * rs) @ v
+    return o, m + np.log(l)
+
+
+def backward_dropout_head(q, k, v, do, keep, t: int, causal: bool = False, scale: Optional[float] = None):
+    """Chain-rule backward of :func:`forward_dropout_head` for one head.
+
+    With Pd = P o Z / (1 - t/256) and O = Pd V:
+      dV = Pd^T dO
+      dP = (dO V^T) o Z / (1 - t/256)      (gradient reaching P through the mask)
+      D_i = P_i:^T dP_i:                   (= do_i . o_i, as without dropout)
+      dS = P o (dP - D)
+      dQ = scale * dS K,   dK = scale * dS^T Q
+    Returns (dQ, dK, dV).
+    """
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    s = scores(q, k, scale, causal)
+    p, _, _ = softmax_stats(s)
+    rs = 256.0 / (256.0 - t)
+    zr = keep * rs
+    dv = (p * zr).T @ do
+    dp = (do @ v.T) * zr
+    dsum = np.sum(p * dp, axis=-1)
+    ds = p * (dp - dsum[:, None])
+    return scale * (ds @ k), scale * (ds.T @ q), dv
+
+
+def finite_difference_grads_dropout(q, k, v, g, keep, t: int, causal: bool = False,
+                                    scale: Optional[float] = None, h: float = 1e-6):
+    """Central differences of sum(O * G) for the dropout forward with a fixed
+    keep mask (tiny problems only); see :func:`finite_difference_grads`."""
+    q, k, v, g = _as_f64(q).copy(), _as_f64(k).copy(), _as_f64(v).copy(), _as_f64(g)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+
+    def phi():
+        o, _ = forward_dropout_head(q, k, v, keep, t, causal, scale)
+        return float(np.sum(o * g))
+
+    grads = []
+    for x in (q, k, v):
+        gx = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            keep_val = x[idx]
+            x[idx] = keep_val + h
+            up = phi()
+            x[idx] = keep_val - h
+            dn = phi()
+            x[idx] = keep_val
+            gx[idx] = (up - dn) / (2.0 * h)
+        grads.append(gx)
+    return tuple(grads)

@@ -534,3 +534,156 @@ def test_merge_of_two_blocks_is_the_tiling_identity():
     m = max(parts_l)
     bad = sum(math.exp(m - l) * po for l, po in zip(parts_l, parts_o))
     assert not np.allclose(bad / sum(math.exp(m - l) for l in parts_l), o[0], atol=1e-6)
+
+
+# --- dropout: Philox4x32-10 and the regenerated mask ----------------------
+
+KAT = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.json")
+
+
+def test_philox_known_answer_vectors():
+    with open(KAT) as f:
+        kat = json.load(f)
+    for vec in kat["vectors"]:
+        ctr = [int(x, 16) for x in vec["counter"]]
+        key = [int(x, 16) for x in vec["key"]]
+        out = ref.philox4x32(ctr, key)
+        assert [int(x) for x in out] == [int(x, 16) for x in vec["output"]]
+    # vectorised over a batch of counters gives the same as one at a time
+    ctrs = np.array([[int(x, 16) for x in v["counter"]] for v in kat["vectors"]], dtype=np.uint64)
+    keys = np.array([[int(x, 16) for x in v["key"]] for v in kat["vectors"]], dtype=np.uint64)
+    batch = ref.philox4x32(ctrs, keys)
+    assert [[int(x) for x in row] for row in batch] == [[int(x, 16) for x in v["output"]] for v in kat["vectors"]]
+
+
+@pytest.mark.parametrize("p,t", [(0.0, 0), (0.1, 26), (0.25, 64), (0.5, 128), (0.99, 253), (255 / 256, 255)])
+def test_dropout_threshold_rounding(p, t):
+    assert ref.dropout_threshold(p) == t
+
+
+@pytest.mark.parametrize("p", [-0.01, 1.0, 0.999])
+def test_dropout_threshold_rejects_out_of_range(p):
+    with pytest.raises(ValueError):
+        ref.dropout_threshold(p)
+
+
+@pytest.mark.parametrize("t", [0, 1, 26, 128, 255])
+def test_dropout_keep_rate_matches_threshold(t):
+    keep = ref.dropout_keep_mask(3, 384, 512, seed=0x1234_5678_9ABC, offset=7, t=t)
+    n = keep.size
+    want = 1.0 - t / 256.0
+    sigma = math.sqrt(want * (1.0 - want) / n)
+    assert abs(keep.mean() - want) <= 5 * sigma + 1e-12
+    if t == 0:
+        assert keep.all()
+
+
+def test_dropout_mask_bytes_are_uniform():
+    # the byte each element draws: 256 equally likely values (chi-square, 255 dof, p ~ 1e-6 bound)
+    keep_prev = ref.dropout_keep_mask(0, 256, 256, seed=99, offset=0, t=0)
+    assert keep_prev.all()
+    # recover each element's byte as the largest t that still keeps it (binary search over t)
+    lo = np.zeros((256, 256), dtype=np.int64)
+    hi = np.full((256, 256), 256, dtype=np.int64)
+    for _ in range(8):
+        mid = (lo + hi) // 2
+        keep = np.zeros((256, 256), dtype=bool)
+        for t in np.unique(mid):
+            sel = mid == t
+            keep[sel] = ref.dropout_keep_mask(0, 256, 256, seed=99, offset=0, t=int(min(t, 255)))[sel]
+        lo = np.where(keep, mid, lo)
+        hi = np.where(keep, hi, mid)
+    counts = np.bincount(lo.ravel(), minlength=256)
+    expected = lo.size / 256.0
+    chi2 = float(np.sum((counts - expected) ** 2 / expected))
+    assert chi2 < 255 + 6 * math.sqrt(2 * 255)
+
+
+def test_dropout_mask_is_a_function_of_seed_offset_and_head():
+    a = ref.dropout_keep_mask(5, 64, 96, seed=42, offset=3, t=128)
+    assert np.array_equal(a, ref.dropout_keep_mask(5, 64, 96, seed=42, offset=3, t=128))
+    for other in (ref.dropout_keep_mask(6, 64, 96, seed=42, offset=3, t=128),
+                  ref.dropout_keep_mask(5, 64, 96, seed=43, offset=3, t=128),
+                  ref.dropout_keep_mask(5, 64, 96, seed=42 + (1 << 32), offset=3, t=128),
+                  ref.dropout_keep_mask(5, 64, 96, seed=42, offset=4, t=128)):
+        agree = float(np.mean(a == other))
+        assert 0.4 < agree < 0.6           # independent halves agree half the time
+    # a sub-rectangle of a larger mask is the mask of the smaller problem (position-keyed)
+    big = ref.dropout_keep_mask(5, 100, 130, seed=42, offset=3, t=128)
+    assert np.array_equal(big[:64, :96], a)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_with_t0_is_plain_attention(causal):
+    n, d = 13, 8
+    q, k, v, do = (_rand((n, d), s) for s in (1, 2, 3, 4))
+    keep = np.ones((n, n), dtype=bool)
+    o, lse = ref.forward_dropout_head(q, k, v, keep, 0, causal, 0.4)
+    o2, lse2 = ref.forward_head(q, k, v, causal, 0.4)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+    for a, b in zip(ref.backward_dropout_head(q, k, v, do, keep, 0, causal, 0.4),
+                    ref.backward_head(q, k, v, do, causal, 0.4)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-15)
+
+
+def _torch_dropout_attention(q, k, v, keep, t, causal, scale):
+    """Dropout attention composed from torch float64 ops (autograd differentiates it)."""
+    s = scale * (q @ k.T)
+    if causal:
+        n = s.shape[0]
+        s = s.masked_fill(torch.ones(n, s.shape[1], dtype=torch.bool).triu(1), float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    return (p * torch.from_numpy(keep.astype(np.float64)) / (1.0 - t / 256.0)) @ v, torch.logsumexp(s, dim=-1)
+
+
+@pytest.mark.parametrize("causal,t", [(False, 26), (True, 26), (True, 128)])
+def test_dropout_forward_backward_match_torch_autograd_float64(causal, t):
+    n, d = 24, 16
+    q, k, v, do = (_rand((n, d), s) for s in (11, 12, 13, 14))
+    keep = ref.dropout_keep_mask(2, n, n, seed=7, offset=1, t=t)
+    assert 0 < keep.sum() < keep.size
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    o_t, lse_t = _torch_dropout_attention(tq, tk, tv, keep, t, causal, 0.3)
+    o_t.backward(torch.from_numpy(do))
+    o, lse = ref.forward_dropout_head(q, k, v, keep, t, causal, 0.3)
+    np.testing.assert_allclose(o, o_t.detach().numpy(), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_t.detach().numpy(), rtol=0, atol=1e-13)
+    dq, dk, dv = ref.backward_dropout_head(q, k, v, do, keep, t, causal, 0.3)
+    for mine, theirs in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(mine, theirs.numpy(), rtol=0, atol=1e-12)
+
+
+def test_dropout_backward_matches_finite_differences():
+    n, d = 6, 3
+    q, k, v, g = (_rand((n, d), s) for s in (21, 22, 23, 24))
+    keep = ref.dropout_keep_mask(0, n, n, seed=5, offset=0, t=100)
+    want = ref.finite_difference_grads_dropout(q, k, v, g, keep, 100, True, 0.7)
+    got = ref.backward_dropout_head(q, k, v, g, keep, 100, True, 0.7)
+    for a, b in zip(got, want):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-7)
+
+
+def test_dropout_is_unbiased_in_expectation():
+    # averaging O over many independent masks approaches the undropped O (E[Z] / (1 - t/256) = 1)
+    n, d, t = 8, 4, 64
+    q, k, v = (_rand((n, d), s) for s in (31, 32, 33))
+    o_ref, _ = ref.forward_head(q, k, v, True, 0.5)
+    samples = np.stack([ref.forward_dropout_head(q, k, v, ref.dropout_keep_mask(0, n, n, 77, off, t), t, True, 0.5)[0]
+                        for off in range(3000)])
+    mean, std = samples.mean(axis=0), samples.std(axis=0)
+    assert np.all(np.abs(mean - o_ref) <= 5 * std / math.sqrt(len(samples)) + 1e-12)
+
+
+def test_dropout_pins_catch_an_unmasked_dp():
+    # a planted mistake in the oracle's own arithmetic (the mask left off dP) fails the autograd pin
+    n, d, t = 16, 8, 64
+    q, k, v, do = (_rand((n, d), s) for s in (41, 42, 43, 44))
+    keep = ref.dropout_keep_mask(1, n, n, seed=3, offset=0, t=t)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    o_t, _ = _torch_dropout_attention(tq, tk, tv, keep, t, False, 0.5)
+    o_t.backward(torch.from_numpy(do))
+    p, _, _ = ref.softmax_stats(ref.scores(q, k, 0.5, False))
+    dp_wrong = do @ v.T                                  # mistake: no keep mask, no 1/(1 - p)
+    ds = p * (dp_wrong - np.sum(p * dp_wrong, axis=-1)[:, None])
+    assert np.max(np.abs(0.5 * ds @ k - tq.grad.numpy())) > 1e-3
