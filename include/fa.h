@@ -65,7 +65,8 @@ enum fa_status {
   FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than fa_backward_workspace_size */
   FA_ERR_HIP = 7,       /* the HIP runtime reported an error at launch */
   FA_ERR_ALIGN = 8,     /* a tensor pointer is not 16-byte aligned */
-  FA_ERR_MASK = 9       /* block-sparse mask geometry invalid (see fa_forward_block_sparse) */
+  FA_ERR_MASK = 9,      /* block-sparse mask geometry invalid (see fa_forward_block_sparse) */
+  FA_ERR_DROPOUT = 10   /* dropout probability outside [0, 255/256] after rounding (see fa_forward_dropout) */
 };
 
 /*
@@ -154,6 +155,34 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
                 int B, int H, int N, int d, int causal, float scale, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Attention with dropout on the probabilities, forward and backward
+ * ("Как работает FlashAttention математически", section 5; "Overview of
+ * Flash Attention series", Backward Pass: masks are regenerated, not stored):
+ *   O = (P o Z) V / (1 - t/256),  P = softmax(scale * Q K^T),
+ * lse that of the undropped scores.  The keep mask Z is a pure function of
+ * (seed, offset, b * H + h, query, key), so the backward, called with the
+ * same seed and offset, regenerates it: element (i, j) of head bh takes
+ * byte 4 (i mod 4) + (j mod 4) (little-endian within the words) of the
+ * counter-based generator Philox4x32-10 (Salmon et al., SC 2011) at counter
+ * (j / 4, i / 4, bh, offset) with key (seed low word, seed high word), and is
+ * dropped when that byte is < t.  The drop probability p_drop is quantised
+ * to t / 256 with t = floor(256 p_drop + 0.5) in float32; t outside [0, 255]
+ * (or a non-finite p_drop) returns FA_ERR_DROPOUT.  t = 0 is attention
+ * without dropout.  The backward uses
+ *   dV = (P o Z)^T dO / (1 - t/256),  dS = P o (dP o Z / (1 - t/256) - D),
+ * with D_i = do_i . o_i as without dropout.  Everything else as fa_forward
+ * and fa_backward.
+ */
+int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, int causal, float scale, int dtype,
+                       float p_drop, unsigned long long seed, unsigned offset, void* stream);
+int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        int B, int H, int N, int d, int causal, float scale, int dtype,
+                        float p_drop, unsigned long long seed, unsigned offset,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The three stages that fa_backward enqueues, in order, for callers that

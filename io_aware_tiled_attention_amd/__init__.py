@@ -16,13 +16,15 @@ import math
 from typing import Optional, Tuple
 
 from . import _lib
-from ._lib import (FA_BF16, FA_F32, FaError, fa_backward, fa_backward_dkdv, fa_backward_dq,
+from ._lib import (FA_BF16, FA_F32, FaError, fa_backward, fa_backward_dkdv, fa_backward_dq, fa_backward_dropout,
                    fa_backward_preprocess, fa_backward_workspace_size, fa_decode, fa_decode_num_splits,
-                   fa_decode_workspace_size, fa_forward, fa_forward_block_sparse, fa_strerror)
+                   fa_decode_workspace_size, fa_forward, fa_forward_block_sparse, fa_forward_dropout,
+                   fa_strerror)
 
 __all__ = ["forward", "forward_block_sparse", "backward", "decode", "workspace_size", "FaError", "FA_F32",
            "FA_BF16", "fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_size",
-           "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_decode",
+           "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_forward_dropout",
+           "fa_backward_dropout", "fa_decode",
            "fa_decode_workspace_size", "fa_decode_num_splits", "fa_strerror", "load_library",
            "backward_stages"]
 
@@ -58,8 +60,13 @@ def _stream_ptr(device) -> int:
 
 
 def forward(q, k, v, causal: bool = False, scale: Optional[float] = None,
-            out=None, lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
-    """O = softmax(scale * Q K^T) V and lse = ln rowsum exp(scale * Q K^T)."""
+            out=None, lse=None, dropout_p: float = 0.0, seed: int = 0,
+            offset: int = 0) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """O = softmax(scale * Q K^T) V and lse = ln rowsum exp(scale * Q K^T).
+
+    ``dropout_p`` > 0: dropout on the probabilities, O = (P o Z) V / (1 - t/256)
+    with t = round(256 dropout_p); the mask Z is regenerated from (seed,
+    offset), so :func:`backward` must get the same three values."""
     import torch
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
@@ -76,6 +83,13 @@ def forward(q, k, v, causal: bool = False, scale: Optional[float] = None,
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check("out", out, q.shape, q.dtype, q.device)
     _check("lse", lse, (B, H, N), torch.float32, q.device)
+    if dropout_p:
+        st = fa_forward_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                B, H, N, d, causal, scale, _dtype_code(q), dropout_p, seed, offset,
+                                _stream_ptr(q.device))
+        if st != 0:
+            raise FaError(st, "fa_forward_dropout")
+        return out, lse
     st = fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                     B, H, N, d, causal, scale, _dtype_code(q), _stream_ptr(q.device))
     if st != 0:
@@ -166,8 +180,10 @@ def workspace_size(B: int, H: int, N: int, d: int) -> int:
 
 
 def backward(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
-             dq=None, dk=None, dv=None, workspace=None):
-    """dQ, dK, dV of O = attention(Q, K, V) for the upstream gradient dO."""
+             dq=None, dk=None, dv=None, workspace=None, dropout_p: float = 0.0, seed: int = 0,
+             offset: int = 0):
+    """dQ, dK, dV of O = attention(Q, K, V) for the upstream gradient dO
+    (with dropout: the same dropout_p, seed and offset as the forward)."""
     import torch
     B, H, N, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
@@ -183,6 +199,14 @@ def backward(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] =
     need = fa_backward_workspace_size(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if dropout_p:
+        st = fa_backward_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                                 causal, scale, _dtype_code(q), dropout_p, seed, offset, workspace.data_ptr(),
+                                 workspace.numel(), _stream_ptr(q.device))
+        if st != 0:
+            raise FaError(st, "fa_backward_dropout")
+        return dq, dk, dv
     st = fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
                      causal, scale, _dtype_code(q), workspace.data_ptr(), workspace.numel(),

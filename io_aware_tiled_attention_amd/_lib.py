@@ -18,10 +18,11 @@ FA_F32 = 0
 FA_BF16 = 1
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_DTYPE",
-    5: "FA_ERR_SCALE", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ALIGN", 9: "FA_ERR_MASK",
+    5: "FA_ERR_SCALE", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ALIGN", 9: "FA_ERR_MASK", 10: "FA_ERR_DROPOUT",
 }
 EXPORTED = ("fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_size",
-            "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_decode",
+            "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_forward_dropout",
+            "fa_backward_dropout", "fa_decode",
             "fa_decode_workspace_size", "fa_decode_num_splits", "fa_strerror")
 
 _lock = threading.Lock()
@@ -62,6 +63,12 @@ def load() -> ctypes.CDLL:
         lib.fa_backward_dkdv.restype = i
         lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
         lib.fa_backward_dq.restype = i
+        u64, u32 = ctypes.c_uint64, ctypes.c_uint32
+        lib.fa_forward_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, u64, u32, vp]
+        lib.fa_forward_dropout.restype = i
+        lib.fa_backward_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, u64, u32,
+                                            vp, sz, vp]
+        lib.fa_backward_dropout.restype = i
         lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
         lib.fa_decode.restype = i
         lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i]
@@ -108,6 +115,18 @@ def fa_backward_dq(q, k, v, dout, dq, B, H, N, d, causal, scale, dtype,
 
 def fa_backward_workspace_size(B, H, N, d) -> int:
     return load().fa_backward_workspace_size(B, H, N, d)
+
+
+def fa_forward_dropout(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, p_drop, seed, offset, stream) -> int:
+    return load().fa_forward_dropout(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), dtype, float(p_drop),
+                                     int(seed), int(offset), stream)
+
+
+def fa_backward_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype, p_drop, seed, offset,
+                        workspace, workspace_bytes, stream) -> int:
+    return load().fa_backward_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, int(causal), float(scale),
+                                      dtype, float(p_drop), int(seed), int(offset), workspace, workspace_bytes,
+                                      stream)
 
 
 def fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, num_splits,

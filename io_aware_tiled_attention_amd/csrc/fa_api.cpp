@@ -38,7 +38,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 // or writes it.
 int run_backward(int stages, const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal,
-                 float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                 float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                 const fa::DropParams& drop = fa::DropParams{}) {
   bool empty = false;
   const int st = check_shape(B, H, N, d, dtype, scale, &empty);
   if (st != FA_OK) return st;
@@ -69,8 +70,23 @@ int run_backward(int stages, const void* q, const void* k, const void* v, const 
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_ALIGN;
   char* ws = static_cast<char*>(workspace);
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal ? 1 : 0, dtype, scale,
-                reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + fa::ws_dsum_bytes(rows))};
+                reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + fa::ws_dsum_bytes(rows)), drop};
   return hip_status(fa::launch_backward(a, stages, static_cast<hipStream_t>(stream)));
+}
+
+// Dropout parameters: t = round(256 p) (float32 product, half away from
+// zero) must lie in [0, 255]; t = 0 leaves dropout off (the plain kernels).
+int make_drop(float p_drop, unsigned long long seed, unsigned offset, fa::DropParams* out) {
+  if (!std::isfinite(p_drop)) return FA_ERR_DROPOUT;
+  const float t = std::floor(p_drop * 256.0f + 0.5f);
+  if (t < 0.f || t > 255.f) return FA_ERR_DROPOUT;
+  out->k0 = (unsigned)(seed & 0xFFFFFFFFull);
+  out->k1 = (unsigned)(seed >> 32);
+  out->offset = offset;
+  out->t = (unsigned)t;
+  out->rs = 256.0f / (256.0f - t);
+  out->on = out->t > 0;
+  return FA_OK;
 }
 
 }  // namespace
@@ -86,6 +102,23 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
   fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal ? 1 : 0, dtype, scale};
+  return hip_status(fa::launch_forward(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                       int d, int causal, float scale, int dtype, float p_drop, unsigned long long seed,
+                       unsigned offset, void* stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, dtype, scale, &empty);
+  if (st != FA_OK) return st;
+  fa::DropParams drop;
+  st = make_drop(p_drop, seed, offset, &drop);
+  if (st != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal ? 1 : 0, dtype, scale};
+  a.drop = drop;
   return hip_status(fa::launch_forward(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -178,6 +211,21 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                       d, causal, scale, dtype, workspace, workspace_bytes, stream);
 }
 
+int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal,
+                        float scale, int dtype, float p_drop, unsigned long long seed, unsigned offset,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  fa::DropParams drop;
+  const int st = make_drop(p_drop, seed, offset, &drop);
+  if (st != FA_OK) {
+    bool empty = false;
+    const int shape = check_shape(B, H, N, d, dtype, scale, &empty);
+    return shape != FA_OK ? shape : st;
+  }
+  return run_backward(fa::kStagePre | fa::kStageDkDv | fa::kStageDq, q, k, v, o, dout, lse, dq, dk, dv, B, H, N,
+                      d, causal, scale, dtype, workspace, workspace_bytes, stream, drop);
+}
+
 int fa_backward_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int N, int d, int dtype,
                            void* workspace, size_t workspace_bytes, void* stream) {
   return run_backward(fa::kStagePre, nullptr, nullptr, nullptr, o, dout, lse, nullptr, nullptr, nullptr, B, H, N, d,
@@ -212,6 +260,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_MASK:
       return "invalid block mask geometry: mask_heads must be 1 or H, block_q a positive multiple of 32, "
              "block_k a positive multiple of 64, and N at most 65536";
+    case FA_ERR_DROPOUT: return "invalid dropout probability: round(256 p) must lie in [0, 255]";
     default: return "unknown fa_status";
   }
 }

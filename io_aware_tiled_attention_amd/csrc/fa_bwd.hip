@@ -92,11 +92,11 @@ void fa_bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, const 
 }
 
 // ---------------------------------------------------------------- 2. dK, dV
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kBwdThreads, 2)
 void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                         const T* __restrict__ dO, const float* __restrict__ dsum, const float* __restrict__ nlse,
-                        T* __restrict__ dK, T* __restrict__ dV, int N, int BH, float scale) {
+                        T* __restrict__ dK, T* __restrict__ dV, int N, int BH, float scale, DropParams dpar) {
   using M = Mfma<T>;
   using C = BwdCfg<T, D>;
   using G = Tile<T, D>;                 // Q and dO tiles: BQ rows x D
@@ -128,6 +128,8 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
   const rsrc_t rnl = make_rsrc(nlse + (size_t)bh * N, (uint32_t)N * 4u);
   const rsrc_t rdd = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
   const float kfac = X::factor(scale);
+  int q_blk = 0;   // first query row of the current block (dropout counters)
+  if constexpr (!DROP) (void)dpar;
 
   // K and V rows of this wave as B operands (column = key, KPL d-values of group g).
   Frag kf[D / KC], vf[D / KC];
@@ -174,8 +176,13 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
   };
   // P = ex(S*factor - lse) and dS = P (dP - D) in place; with `lim` >= 0
   // entries whose row offset acc_row(i, 0) < lim (key > query) get P = 0.
+  // DROP: the P kept for dV is P o Z (1 / (1 - t/256) applied at the end),
+  // and dS = P (dP o Z / (1 - t/256) - D).
   auto softmax_grad = [&](const lds_u8* nl_s, const lds_u8* dd_s, int qs_i, f32x16& s, f32x16& dp, bool masked,
                           int lim) {
+    u32x4 rb = {};
+    if constexpr (DROP)
+      rb = drop_bytes_queries(dpar.k0, dpar.k1, dpar.offset, (unsigned)bh, mykey, q_blk + qs_i * 32, g, lane);
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const f32x4 lz = *(const lds_f32x4*)(nl_s + (qs_i * 32 + 8 * a + 4 * g) * 4);
@@ -185,8 +192,14 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
         const int i = 4 * a + b;
         float p = X::ex(__builtin_fmaf(s[i], kfac, lz[b]));
         if (masked) p = (acc_row(i, 0) < lim) ? 0.f : p;
-        s[i] = p;
-        dp[i] = p * (dp[i] - dz[b]);
+        if constexpr (DROP) {
+          const bool keep = drop_keep(rb, i, dpar.t);
+          s[i] = keep ? p : 0.f;
+          dp[i] = p * ((keep ? dp[i] * dpar.rs : 0.f) - dz[b]);
+        } else {
+          s[i] = p;
+          dp[i] = p * (dp[i] - dz[b]);
+        }
       }
     }
   };
@@ -227,6 +240,7 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
 
   for (int it = 0; it < nblocks; ++it) {
     const int q0b = q_begin + it * BQ;
+    q_blk = q0b;
     const int st = it & 1;
     if (it + 1 < nblocks) load_block(q0b + BQ, st ^ 1);
 
@@ -263,7 +277,9 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
       const int off = mykey * G::R + (db * 32 + 8 * a + 4 * g) * (int)sizeof(T);
       store4<T>(rdk, off, dk_acc[db][4 * a] * scale, dk_acc[db][4 * a + 1] * scale, dk_acc[db][4 * a + 2] * scale,
                 dk_acc[db][4 * a + 3] * scale);
-      store4<T>(rdv, off, dv_acc[db][4 * a], dv_acc[db][4 * a + 1], dv_acc[db][4 * a + 2], dv_acc[db][4 * a + 3]);
+      const float vs = DROP ? dpar.rs : 1.f;
+      store4<T>(rdv, off, dv_acc[db][4 * a] * vs, dv_acc[db][4 * a + 1] * vs, dv_acc[db][4 * a + 2] * vs,
+                dv_acc[db][4 * a + 3] * vs);
     }
 }
 
@@ -303,12 +319,12 @@ struct KvCfg {
   static_assert(STAGE + DO0 + 16 * G::R < 65536, "stage offsets fit the ds_read immediate");
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kKvThreads, 1)
 void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                              const bf16* __restrict__ dO, const float* __restrict__ dsum,
                              const float* __restrict__ nlse, bf16* __restrict__ dK, bf16* __restrict__ dV, int N,
-                             int BH, float scale) {
+                             int BH, float scale, DropParams dpar) {
   using M = Mfma<bf16>;
   using C = KvCfg<D>;
   using G = Tile<bf16, D>;
@@ -347,6 +363,7 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
   const u32x4 rnl = rsrc_words(nlse + (size_t)bh * N, (uint32_t)N * 4u);
   const u32x4 rdd = rsrc_words(dsum + (size_t)bh * N, (uint32_t)N * 4u);
   const float kfac = X::factor(scale);
+  if constexpr (!DROP) (void)dpar;
 
   // Loop-invariant per-lane LDS offsets.  The swizzle depends on the row
   // modulo 16 only, so an offset computed for rows 0..31 holds for every
@@ -433,6 +450,10 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
       // P = ex(S*factor - lse), dS = P (dP - D); masked (key > query, or a key
       // past the end) -> P = 0.
       const int lim = (mykey >= N) ? 64 : (CAUSAL ? mykey - (qsb + 4 * g) : -1);
+      // DROP: P o Z for dV (1 / (1 - t/256) applied at the end), and
+      // dS = P (dP o Z / (1 - t/256) - D).
+      u32x4 rb = {};
+      if constexpr (DROP) rb = drop_bytes_queries(dpar.k0, dpar.k1, dpar.offset, (unsigned)bh, mykey, qsb, g, lane);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const f32x4 lz = *(const lds_f32x4*)(sb + C::NL0 + stat_off + 32 * a);
@@ -444,8 +465,14 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
           if constexpr (MASKED) {
             if (diag) p = (acc_row(i, 0) < lim) ? 0.f : p;
           }
-          s[i] = p;
-          dp[i] = p * (dp[i] - dz[b]);
+          if constexpr (DROP) {
+            const bool keep = drop_keep(rb, i, dpar.t);
+            s[i] = keep ? p : 0.f;
+            dp[i] = p * ((keep ? dp[i] * dpar.rs : 0.f) - dz[b]);
+          } else {
+            s[i] = p;
+            dp[i] = p * (dp[i] - dz[b]);
+          }
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows.
@@ -534,8 +561,9 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
                      (dk_acc[db][4 * a + 2] + o[2]) * scale, (dk_acc[db][4 * a + 3] + o[3]) * scale);
       } else {
         const f32x4 o = *(const lds_f32x4*)(xv + xo);
-        store4<bf16>(rdv, off, dv_acc[db][4 * a] + o[0], dv_acc[db][4 * a + 1] + o[1], dv_acc[db][4 * a + 2] + o[2],
-                     dv_acc[db][4 * a + 3] + o[3]);
+        const float vs = DROP ? dpar.rs : 1.f;
+        store4<bf16>(rdv, off, (dv_acc[db][4 * a] + o[0]) * vs, (dv_acc[db][4 * a + 1] + o[1]) * vs,
+                     (dv_acc[db][4 * a + 2] + o[2]) * vs, (dv_acc[db][4 * a + 3] + o[3]) * vs);
       }
     }
 }
@@ -547,11 +575,11 @@ constexpr int kDqBR = kDqWaves * kDqQW;         // query rows per workgroup
 constexpr int kDqBC = 64;                       // keys per K/V tile
 constexpr int kDqThreads = kDqWaves * 64;
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kDqThreads, sizeof(T) == 2 ? 2 : 1)
 void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                       const T* __restrict__ dO, const float* __restrict__ dsum, const float* __restrict__ nlse,
-                      T* __restrict__ dQ, int N, int BH, int n_qtiles, float scale) {
+                      T* __restrict__ dQ, int N, int BH, int n_qtiles, float scale, DropParams dpar) {
   using M = Mfma<T>;
   using G = Tile<T, D>;
   using X = ExpDomain<T>;
@@ -596,6 +624,7 @@ void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
   const rsrc_t rdd = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
   const float nl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rnl, myq * 4, 0, 0));
   const float dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdd, myq * 4, 0, 0));
+  if constexpr (!DROP) (void)dpar;
 
   const int kv_end = CAUSAL ? min(N, q0 + kDqBR) : N;
   const int ntiles = (kv_end + kDqBC - 1) / kDqBC;
@@ -648,13 +677,19 @@ void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
         }
       }
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb) {
+        // DROP: dS = P (dP o Z / (1 - t/256) - D)
+        u32x4 rb = {};
+        if constexpr (DROP)
+          rb = drop_bytes_keys(dpar.k0, dpar.k1, dpar.offset, (unsigned)bh, myq, kv0 + kb * 32, g, lane);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           // masked scores are -inf and kfac > 0, so P = 0 there
           const float p = X::ex(__builtin_fmaf(s[kb][i], kfac, nl));
-          dp[kb][i] = p * (dp[kb][i] - dd);
+          if constexpr (DROP) dp[kb][i] = p * ((drop_keep(rb, i, dpar.t) ? dp[kb][i] * dpar.rs : 0.f) - dd);
+          else dp[kb][i] = p * (dp[kb][i] - dd);
         }
+      }
       // dQ^T += K^T dS^T, dS^T straight from registers (B operand), K^T from
       // the K tile through the transpose read (A operand).
 #pragma unroll
@@ -692,12 +727,12 @@ void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
 // The two 32-key halves of a tile are processed one after the other so that
 // the first half's dS is already packed to bf16 while the second half's
 // products run.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kDqThreads, 2)
 void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                            const bf16* __restrict__ dO, const float* __restrict__ dsum,
                            const float* __restrict__ nlse, bf16* __restrict__ dQ, int N, int BH, int n_qtiles,
-                           float scale) {
+                           float scale, DropParams dpar) {
   using M = Mfma<bf16>;
   using G = Tile<bf16, D>;
   using X = ExpDomain<bf16>;
@@ -746,6 +781,7 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   const rsrc_t rdd = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
   const float nl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rnl, myq * 4, 0, 0));
   const float dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdd, myq * 4, 0, 0));
+  if constexpr (!DROP) (void)dpar;
 
   // Loop-invariant per-lane LDS offsets (the swizzle depends on the row
   // modulo 16 only): ka[c] = row r32, k-chunk c of a tile; tk[db][e] = the
@@ -820,10 +856,15 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
             for (int i = 0; i < 16; ++i) s[i] = (acc_row(i, 0) > lim) ? kNegInf : s[i];
           }
         }
+        // DROP: dS = P (dP o Z / (1 - t/256) - D)
+        u32x4 rb = {};
+        if constexpr (DROP)
+          rb = drop_bytes_keys(dpar.k0, dpar.k1, dpar.offset, (unsigned)bh, myq, kv0 + kb * 32, g, lane);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = X::ex(__builtin_fmaf(s[i], kfac, nl));
-          dp[i] = p * (dp[i] - dd);
+          if constexpr (DROP) dp[i] = p * ((drop_keep(rb, i, dpar.t) ? dp[i] * dpar.rs : 0.f) - dd);
+          else dp[i] = p * (dp[i] - dd);
         }
         ds[0] = M::pack(dp, 0);
         ds[1] = M::pack(dp, 1);
@@ -892,7 +933,7 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
                    acc[db][4 * a + 1] * scale, acc[db][4 * a + 2] * scale, acc[db][4 * a + 3] * scale);
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool DROP>
 hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   const int BH = a.B * a.H;
   const size_t rows = (size_t)BH * a.N;
@@ -908,39 +949,39 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   }
   if (stages & kStageDkDv) {
     if constexpr (sizeof(T) == 2) {
-      hipLaunchKernelGGL((fa_bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3(n_ktiles * BH), dim3(kKvThreads), 0, stream,
-                         static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
-                         static_cast<const bf16*>(a.dout), a.dsum, a.nlse, static_cast<bf16*>(a.dk),
-                         static_cast<bf16*>(a.dv), a.N, BH, a.scale);
+      hipLaunchKernelGGL((fa_bwd_dkdv_bf16_kernel<D, CAUSAL, DROP>), dim3(n_ktiles * BH), dim3(kKvThreads), 0,
+                         stream, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                         static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.dsum, a.nlse,
+                         static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, BH, a.scale, a.drop);
     } else {
       using C = BwdCfg<T, D>;
-      auto kern = fa_bwd_dkdv_kernel<T, D, CAUSAL>;
+      auto kern = fa_bwd_dkdv_kernel<T, D, CAUSAL, DROP>;
       static const hipError_t attr_err =
           hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::BYTES);
       if (attr_err != hipSuccess) return attr_err;
       hipLaunchKernelGGL(kern, dim3(n_ktiles * BH), dim3(kBwdThreads), C::BYTES, stream,
                          static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                          static_cast<const T*>(a.dout), a.dsum, a.nlse, static_cast<T*>(a.dk),
-                         static_cast<T*>(a.dv), a.N, BH, a.scale);
+                         static_cast<T*>(a.dv), a.N, BH, a.scale, a.drop);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & kStageDq) {
     if constexpr (sizeof(T) == 2) {
-      hipLaunchKernelGGL((fa_bwd_dq_bf16_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(kDqThreads), 0, stream,
-                         static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k), static_cast<const bf16*>(a.v),
-                         static_cast<const bf16*>(a.dout), a.dsum, a.nlse, static_cast<bf16*>(a.dq), a.N, BH,
-                         n_qtiles, a.scale);
+      hipLaunchKernelGGL((fa_bwd_dq_bf16_kernel<D, CAUSAL, DROP>), dim3(n_qtiles * BH), dim3(kDqThreads), 0,
+                         stream, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                         static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.dsum, a.nlse,
+                         static_cast<bf16*>(a.dq), a.N, BH, n_qtiles, a.scale, a.drop);
     } else {
       constexpr int bytes = 4 * kDqBC * D * (int)sizeof(T);
-      auto kern = fa_bwd_dq_kernel<T, D, CAUSAL>;
+      auto kern = fa_bwd_dq_kernel<T, D, CAUSAL, DROP>;
       static const hipError_t attr_err =
           hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
       if (attr_err != hipSuccess) return attr_err;
       hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(kDqThreads), bytes, stream, static_cast<const T*>(a.q),
                          static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<const T*>(a.dout),
-                         a.dsum, a.nlse, static_cast<T*>(a.dq), a.N, BH, n_qtiles, a.scale);
+                         a.dsum, a.nlse, static_cast<T*>(a.dq), a.N, BH, n_qtiles, a.scale, a.drop);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -950,14 +991,15 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
 
 }  // namespace
 
+template <typename T, int D>
+hipError_t launch_bwd_d(const BwdArgs& a, int stages, hipStream_t s) {
+  if (a.causal) return a.drop.on ? launch_bwd_t<T, D, true, true>(a, stages, s) : launch_bwd_t<T, D, true, false>(a, stages, s);
+  return a.drop.on ? launch_bwd_t<T, D, false, true>(a, stages, s) : launch_bwd_t<T, D, false, false>(a, stages, s);
+}
+
 hipError_t launch_backward(const BwdArgs& a, int stages, hipStream_t s) {
-  const bool c = a.causal != 0;
-  if (a.dtype == kDtypeBF16) {
-    if (a.d == 64) return c ? launch_bwd_t<bf16, 64, true>(a, stages, s) : launch_bwd_t<bf16, 64, false>(a, stages, s);
-    return c ? launch_bwd_t<bf16, 128, true>(a, stages, s) : launch_bwd_t<bf16, 128, false>(a, stages, s);
-  }
-  if (a.d == 64) return c ? launch_bwd_t<float, 64, true>(a, stages, s) : launch_bwd_t<float, 64, false>(a, stages, s);
-  return c ? launch_bwd_t<float, 128, true>(a, stages, s) : launch_bwd_t<float, 128, false>(a, stages, s);
+  if (a.dtype == kDtypeBF16) return a.d == 64 ? launch_bwd_d<bf16, 64>(a, stages, s) : launch_bwd_d<bf16, 128>(a, stages, s);
+  return a.d == 64 ? launch_bwd_d<float, 64>(a, stages, s) : launch_bwd_d<float, 128>(a, stages, s);
 }
 
 }  // namespace fa

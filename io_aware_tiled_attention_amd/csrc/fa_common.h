@@ -256,6 +256,80 @@ template <> struct ExpDomain<float> {
   __device__ __forceinline__ static float from_lse(float lse) { return lse; }
 };
 
+// ---------------------------------------------------------------- dropout
+// The dropout mask is never stored: every kernel regenerates the bits it
+// needs from the counter-based generator Philox4x32-10 (Salmon, Moraes,
+// Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011).
+// Element (i, j) of head bh takes byte 4 (i % 4) + (j % 4) of the 16 output
+// bytes (words little-endian) at counter (j / 4, i / 4, bh, offset) with the
+// 64-bit seed as key, and is dropped when that byte is < t.
+
+// One Philox4x32-10 evaluation; the key (k0, k1) is wave-uniform.
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, unsigned k0, unsigned k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const unsigned long long p0 = (unsigned long long)0xD2511F53u * c[0];
+    const unsigned long long p1 = (unsigned long long)0xCD9E8D57u * c[2];
+    c = u32x4{(unsigned)(p1 >> 32) ^ c[1] ^ k0, (unsigned)p1, (unsigned)(p0 >> 32) ^ c[3] ^ k1, (unsigned)p0};
+  }
+  return c;
+}
+
+// Within each quad of lanes (x = lane & 3), lane x holds row x of a 4 x 4
+// matrix of words; returns column x (word a = row a's word x).  Two
+// butterfly stages of quad-permute DPP moves.
+__device__ __forceinline__ unsigned dpp_quad_xor1(unsigned v) {
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ unsigned dpp_quad_xor2(unsigned v) {
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ u32x4 quad_transpose(u32x4 m, int x) {
+  const bool b0 = x & 1, b1 = x & 2;
+  const unsigned r0 = dpp_quad_xor1(b0 ? m[0] : m[1]);
+  const unsigned r1 = dpp_quad_xor1(b0 ? m[2] : m[3]);
+  // column (x & 1) and (x & 1) + 2 of rows (x & ~1) and (x | 1)
+  const unsigned t0 = b0 ? r0 : m[0], t1 = b0 ? m[1] : r0;
+  const unsigned t2 = b0 ? r1 : m[2], t3 = b0 ? m[3] : r1;
+  const unsigned q0 = dpp_quad_xor2(b1 ? t0 : t2);
+  const unsigned q1 = dpp_quad_xor2(b1 ? t1 : t3);
+  return b1 ? u32x4{q0, q1, t2, t3} : u32x4{t0, t1, q0, q1};
+}
+
+// 4 x 4 byte transpose within one lane: byte w of result word y = byte y of word w.
+__device__ __forceinline__ u32x4 byte_transpose(u32x4 w) {
+  const unsigned a = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);   // w0.b0 w1.b0 w0.b1 w1.b1
+  const unsigned b = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);   // w0.b2 w1.b2 w0.b3 w1.b3
+  const unsigned c = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+  const unsigned d = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+  return u32x4{__builtin_amdgcn_perm(c, a, 0x05040100u), __builtin_amdgcn_perm(c, a, 0x07060302u),
+               __builtin_amdgcn_perm(d, b, 0x05040100u), __builtin_amdgcn_perm(d, b, 0x07060302u)};
+}
+
+// Random bytes of the 16 accumulator entries a lane holds for one 32 x 32
+// block, laid out so that entry i is byte (i & 3) of word (i >> 2).
+// Rows along keys (S^T layout: lane = query `qi`, rows = keys k0 + acc_row(i, g)):
+__device__ __forceinline__ u32x4 drop_bytes_keys(unsigned k0s, unsigned k1s, unsigned offset, unsigned bh, int qi,
+                                                 int key0, int g, int lane) {
+  const int x = lane & 3;
+  const u32x4 c = {(unsigned)(key0 / 4 + 2 * x + g), (unsigned)qi >> 2, bh, offset};
+  return quad_transpose(philox4x32_10(c, k0s, k1s), x);
+}
+// Rows along queries (S layout: lane = key `kj`, rows = queries q0 + acc_row(i, g)):
+__device__ __forceinline__ u32x4 drop_bytes_queries(unsigned k0s, unsigned k1s, unsigned offset, unsigned bh, int kj,
+                                                    int q0, int g, int lane) {
+  const int x = lane & 3;
+  const u32x4 c = {(unsigned)kj >> 2, (unsigned)(q0 / 4 + 2 * x + g), bh, offset};
+  return quad_transpose(byte_transpose(philox4x32_10(c, k0s, k1s)), x);
+}
+__device__ __forceinline__ bool drop_keep(const u32x4& bytes, int i, unsigned t) {
+  return ((bytes[i >> 2] >> (8 * (i & 3))) & 0xFFu) >= t;
+}
+
 // Store 4 consecutive fp32 values, rounded to T, at byte offset `off` of a buffer.
 template <typename T>
 __device__ __forceinline__ void store4(rsrc_t r, int off, float a, float b, float c, float d) {

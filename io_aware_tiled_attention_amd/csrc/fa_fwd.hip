@@ -70,11 +70,18 @@ struct FwdSmem {
 // block_q is a multiple of 32 (one mask row per wave) and block_k a multiple
 // of 64 (one mask column per tile), so no tile is partly masked by the block
 // mask.  A row that keeps no key gets O = 0 and lse = -inf.
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+//
+// DROP: dropout on the probabilities ("Как работает FlashAttention
+// математически", section 5; the mask is regenerated, not stored): after
+// the row sum l has taken the undropped P, each entry of a dropped (query,
+// key) pair is zeroed before P V, and O is scaled by 1 / (1 - t/256) in the
+// epilogue; lse is that of the undropped scores.
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1)
 void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                    T* __restrict__ O, float* __restrict__ LSE, int N, int BH, int n_qtiles, float scale,
-                   const unsigned char* __restrict__ mask, int H, int mask_heads, int block_q, int block_k) {
+                   const unsigned char* __restrict__ mask, int H, int mask_heads, int block_q, int block_k,
+                   DropParams dp) {
   using M = Mfma<T>;
   using L = FwdSmem<T, D>;
   using G = Tile<T, D>;
@@ -106,6 +113,7 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   const int qw0 = q0 + w * kFwdQW;
   const int myq = qw0 + r32;
   const float kfac = X::factor(scale);
+  if constexpr (!DROP) (void)dp;
 
   // Q^T as the B operand of S^T = K Q^T: column = query, KPL d-values of group g.
   Frag qf[D / KC];
@@ -262,6 +270,14 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
           psum += p;
         }
       l_run += psum;
+      if constexpr (DROP) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const u32x4 rb = drop_bytes_keys(dp.k0, dp.k1, dp.offset, (unsigned)bh, myq, kv0 + kb * 32, g, lane);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s_cur[kb][i] = drop_keep(rb, i, dp.t) ? s_cur[kb][i] : 0.f;
+        }
+      }
 
       // O^T += V^T P^T, with P^T straight from the registers of S^T.
       const lds_u8* vs = L::v(smem, it & 1);
@@ -294,7 +310,7 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   // a row that kept no key (block-sparse) gets O = 0 and lse = -inf.
   const float l_tot = pair_sum(l_run);
   const bool no_key = !(l_tot > 0.f);
-  const float inv = no_key ? 0.f : 1.f / l_tot;
+  const float inv = no_key ? 0.f : (DROP ? dp.rs : 1.f) / l_tot;
   const rsrc_t ro = make_rsrc(O + head, head_bytes);
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -310,11 +326,11 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, myq * 4, 0, 0);
 }
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   using L = FwdSmem<T, D>;
   constexpr int bytes = L::BYTES + (SPARSE ? kFwdListBytes : 0);
-  auto kern = fa_fwd_kernel<T, D, CAUSAL, SPARSE>;
+  auto kern = fa_fwd_kernel<T, D, CAUSAL, SPARSE, DROP>;
   // raise the dynamic-LDS limit once per instantiation (thread-safe static init)
   static const hipError_t attr_err =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
@@ -324,13 +340,15 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const dim3 grid(n_qtiles * BH), block(kFwdThreads);
   hipLaunchKernelGGL(kern, grid, block, bytes, stream, static_cast<const T*>(a.q),
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<T*>(a.o),
-                     a.lse, a.N, BH, n_qtiles, a.scale, a.mask, a.H, a.mask_heads, a.block_q, a.block_k);
+                     a.lse, a.N, BH, n_qtiles, a.scale, a.mask, a.H, a.mask_heads, a.block_q, a.block_k, a.drop);
   return hipGetLastError();
 }
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_fwd_m(const FwdArgs& a, hipStream_t stream) {
-  return a.mask ? launch_fwd_t<T, D, CAUSAL, true>(a, stream) : launch_fwd_t<T, D, CAUSAL, false>(a, stream);
+  if (a.mask) return launch_fwd_t<T, D, CAUSAL, true, false>(a, stream);
+  if (a.drop.on) return launch_fwd_t<T, D, CAUSAL, false, true>(a, stream);
+  return launch_fwd_t<T, D, CAUSAL, false, false>(a, stream);
 }
 
 }  // namespace

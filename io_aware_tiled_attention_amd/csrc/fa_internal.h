@@ -9,6 +9,16 @@ namespace fa {
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBF16 = 1;
 
+// Dropout on the attention probabilities, its mask regenerated from a
+// counter-based generator (Philox4x32-10 keyed by the seed).
+struct DropParams {
+  unsigned k0 = 0, k1 = 0;   // seed, low and high word
+  unsigned offset = 0;       // fourth counter word
+  unsigned t = 0;            // an element is dropped when its random byte is < t (probability t / 256)
+  float rs = 1.f;            // 1 / (1 - t / 256)
+  bool on = false;
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -20,6 +30,7 @@ struct FwdArgs {
   // block-sparse forward only (mask == nullptr: dense)
   const unsigned char* mask = nullptr;
   int mask_heads = 0, block_q = 0, block_k = 0;
+  DropParams drop{};
 };
 
 constexpr int kSparseMaxN = 65536;   // N limit of the block-sparse forward
@@ -38,6 +49,7 @@ struct BwdArgs {
   float scale;
   float* dsum;     // [B*H*N]   D_i = do_i . o_i          (workspace)
   float* nlse;     // [B*H*N]   -lse_i, exponent domain   (workspace)
+  DropParams drop{};
 };
 
 struct DecArgs {

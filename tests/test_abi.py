@@ -246,3 +246,47 @@ def test_decode_split_count_and_workspace_size():
     assert dec(Nk=64, splits=1, ws=0, ws_bytes=0, q=0) == 1
     assert fa.fa_decode_workspace_size(1, 1, 33, 64, 128, 0) == 0
     assert fa.fa_decode_workspace_size(1, 1, 0, 64, 128, 0) == 0
+
+
+def fwd_drop(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, N=64, d=64, causal=0, scale=0.125,
+             dtype=_lib.FA_BF16, p=0.1, seed=1, offset=0, stream=None)
+    a.update(kw)
+    return fa.fa_forward_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                                 a["causal"], a["scale"], a["dtype"], a["p"], a["seed"], a["offset"], a["stream"])
+
+
+def bwd_drop(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, H=2,
+             N=64, d=64, causal=1, scale=0.125, dtype=_lib.FA_BF16, p=0.1, seed=1, offset=0, ws=0x100000,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return fa.fa_backward_dropout(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                  a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"], a["dtype"], a["p"],
+                                  a["seed"], a["offset"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), 1), (dict(lse=0), 1), (dict(N=-1), 2), (dict(d=32), 3), (dict(dtype=9), 4),
+    (dict(scale=float("nan")), 5), (dict(o=FAKE + 4), 8),
+    (dict(p=1.0), 10), (dict(p=-0.01), 10), (dict(p=float("nan")), 10), (dict(p=float("inf")), 10),
+    (dict(p=0.999), 10),
+    (dict(p=255.4 / 256, q=0), 1),     # rounds to t = 255: accepted, then the NULL q fails
+])
+def test_forward_dropout_rejects_invalid_arguments(kw, status):
+    assert fwd_drop(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dq=0), 1), (dict(ws=0), 6), (dict(N=-2), 2), (dict(p=1.5), 10), (dict(p=-1.0), 10),
+    (dict(p=1.5, N=-2), 2),     # shape errors come first
+    (dict(ws=0x100008), 8),
+])
+def test_backward_dropout_rejects_invalid_arguments(kw, status):
+    assert bwd_drop(**kw) == status
+
+
+def test_dropout_empty_problem_is_a_noop_but_checks_p():
+    assert fwd_drop(N=0, q=0) == 0
+    assert bwd_drop(B=0, q=0) == 0
+    assert fwd_drop(N=0, p=2.0) == 10
