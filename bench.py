@@ -12,7 +12,7 @@ FLOP counting convention: forward 4*B*H*N^2*d, halved when causal; backward
 the wall time of a step, in TFLOP/s.
 
 Prints ONE JSON line.  Options: --gpus N (only 1: the path runs on one GPU),
---steps K, --warmup W, --no-cpu-baseline, --no-extra, --decode-only.
+--steps K, --warmup W, --no-cpu-baseline, --no-extra, --decode-only, --dropout-only.
 """
 from __future__ import annotations
 
@@ -233,6 +233,69 @@ def sparse_measurement(fa, torch, dev, steps):
             "speedup_vs_dense_causal": ms_d / ms_s}
 
 
+def dropout_measurement(fa, torch, dev, steps, p_drop=0.1):
+    """Forward and backward with dropout (mask regenerated from Philox in
+    every kernel) on the 16K causal d=128 shape, against the same calls
+    without dropout.  FLOPs by the same convention (dropout adds none)."""
+    from workloads import PROBLEMS, make_inputs
+    p = PROBLEMS["causal_16k_d128_bwd"]
+    inputs = make_inputs(p, with_do=True)
+    q, k, v, do = (inputs[n].to(dev) for n in ("q", "k", "v", "do"))
+    del inputs
+    o = torch.empty_like(q)
+    lse = torch.empty((p.B, p.H, p.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws_bytes = fa.workspace_size(p.B, p.H, p.N, p.d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    raw = fa.load_library()
+    stream = torch.cuda.current_stream().cuda_stream
+    seed, offset = 0x5EED, 0
+
+    def fwd(drop):
+        if drop:
+            st = raw.fa_forward_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), p.B,
+                                        p.H, p.N, p.d, 1, p.scale, 1, p_drop, seed, offset, stream)
+        else:
+            st = raw.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), p.B, p.H,
+                                p.N, p.d, 1, p.scale, 1, stream)
+        assert st == 0, st
+
+    def bwd(drop):
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), p.B, p.H, p.N, p.d, 1, p.scale, 1)
+        if drop:
+            st = raw.fa_backward_dropout(*args, p_drop, seed, offset, ws.data_ptr(), ws_bytes, stream)
+        else:
+            st = raw.fa_backward(*args, ws.data_ptr(), ws_bytes, stream)
+        assert st == 0, st
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    res = {"workload": f"{p.name} with dropout p={p_drop} (drop probability quantised to "
+                       f"{int(p_drop * 256 + 0.5)}/256)", "p_drop": p_drop}
+    for drop in (True, False):
+        tag = "dropout" if drop else "plain"
+        res[f"{tag}_fwd_ms"] = timed(lambda: fwd(drop))
+        res[f"{tag}_bwd_ms"] = timed(lambda: bwd(drop))
+    res["fwd_tflops"] = p.fwd_flops() / res["dropout_fwd_ms"] * 1e-9
+    res["bwd_tflops"] = p.bwd_flops() / res["dropout_bwd_ms"] * 1e-9
+    res["fwd_frac_peak"] = res["fwd_tflops"] / PEAK_BF16_TFLOPS
+    res["bwd_frac_peak"] = res["bwd_tflops"] / PEAK_BF16_TFLOPS
+    res["fwd_slowdown"] = res["dropout_fwd_ms"] / res["plain_fwd_ms"]
+    res["bwd_slowdown"] = res["dropout_bwd_ms"] / res["plain_bwd_ms"]
+    return res
+
+
 DECODE_SHAPES = [(1, 32, 1, 65536), (8, 32, 1, 8192)]    # (B, H, Nq, Nk), d = 128, bf16, causal
 
 
@@ -321,9 +384,11 @@ def main(argv=None):
     ap.add_argument("--cpu-heads", type=int, default=4, help="whole heads timed on the CPU oracle")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the side measurements (N=4K d=128 fwd+bwd, block-sparse 16K forward, "
-                         "split-KV decoding)")
+                         "split-KV decoding, dropout)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the split-KV decoding measurement (one JSON line; for kernel traces)")
+    ap.add_argument("--dropout-only", action="store_true",
+                    help="only the dropout measurement (one JSON line; for kernel traces)")
     ap.add_argument("--decode-shape", type=int, default=None,
                     help="with --decode-only: only this entry of the decoding shapes")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -355,6 +420,9 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": {"bytes_read_per_copy": 4 * n, "bytes_written_per_copy": 4 * n,
                                                "copies": 3}}), flush=True)
+        return 0
+    if args.dropout_only:
+        print(json.dumps({"dropout_16k_d128": dropout_measurement(fa, torch, dev, max(3, args.steps))}), flush=True)
         return 0
     if args.decode_only:
         shapes = None if args.decode_shape is None else [DECODE_SHAPES[args.decode_shape]]
@@ -391,6 +459,8 @@ def main(argv=None):
         extra["block_sparse_16k_d128"] = sparse_measurement(fa, torch, dev, max(5, args.steps // 2))
         torch.cuda.empty_cache()
         extra["decode_bf16_d128"] = decode_measurement(fa, torch, dev, max(10, args.steps))
+        torch.cuda.empty_cache()
+        extra["dropout_16k_d128"] = dropout_measurement(fa, torch, dev, max(5, args.steps // 2))
 
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

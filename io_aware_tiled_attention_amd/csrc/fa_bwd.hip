@@ -429,6 +429,10 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
     }
     if (run) {
       const lds_u8* sb = smem + ST * C::STAGE;
+      // DROP: this block's random bytes, generated before the products so
+      // that the generator's temporaries are not live next to S and dP.
+      u32x4 rb = {};
+      if constexpr (DROP) rb = drop_bytes_queries(dpar.k0, dpar.k1, dpar.offset, (unsigned)bh, mykey, qsb, g, lane);
       // S = Q K^T and dP = dO V^T: rows = queries, column = this lane's key.
       f32x16 s = f32x16{}, dp = f32x16{};
       Frag fq[2], fd[2], fv[2];
@@ -452,8 +456,6 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
       const int lim = (mykey >= N) ? 64 : (CAUSAL ? mykey - (qsb + 4 * g) : -1);
       // DROP: P o Z for dV (1 / (1 - t/256) applied at the end), and
       // dS = P (dP o Z / (1 - t/256) - D).
-      u32x4 rb = {};
-      if constexpr (DROP) rb = drop_bytes_queries(dpar.k0, dpar.k1, dpar.offset, (unsigned)bh, mykey, qsb, g, lane);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const f32x4 lz = *(const lds_f32x4*)(sb + C::NL0 + stat_off + 32 * a);
@@ -848,7 +850,7 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
       };
       // P = ex(S*factor - lse) (masked scores are -inf and factor > 0, so
       // P = 0 there), dS = P (dP - D), packed to bf16 B fragments.
-      auto softmax = [&](int kb, f32x16& s, f32x16& dp, Frag* ds) {
+      auto softmax = [&](int kb, f32x16& s, f32x16& dp, Frag* ds, const u32x4& rb) {
         if constexpr (MASKED) {
           if (msk) {
             const int lim = last - (kv0 + kb * 32 + 4 * g);
@@ -857,9 +859,6 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
           }
         }
         // DROP: dS = P (dP o Z / (1 - t/256) - D)
-        u32x4 rb = {};
-        if constexpr (DROP)
-          rb = drop_bytes_keys(dpar.k0, dpar.k1, dpar.offset, (unsigned)bh, myq, kv0 + kb * 32, g, lane);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = X::ex(__builtin_fmaf(s[i], kfac, nl));
@@ -891,9 +890,14 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
       Frag ds[NKB][2];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
+        // DROP: the half's random bytes before its products (generator
+        // temporaries not live next to S and dP)
+        u32x4 rb = {};
+        if constexpr (DROP)
+          rb = drop_bytes_keys(dpar.k0, dpar.k1, dpar.offset, (unsigned)bh, myq, kv0 + kb * 32, g, lane);
         f32x16 st, dpt;
         sdp(kb, st, dpt);
-        softmax(kb, st, dpt, ds[kb]);
+        softmax(kb, st, dpt, ds[kb], rb);
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) dq_mma(kb, ds[kb]);
