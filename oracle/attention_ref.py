@@ -71,6 +71,13 @@ the design notes of the repository):
   head bh takes byte 4 (i mod 4) + (j mod 4) (little-endian within the four
   32-bit words) of Philox4x32-10 at counter (j div 4, i div 4, bh, offset)
   with the 64-bit seed as key.
+* FP8 inputs: the pages only name FP8 (for Hopper) without a format or a
+  scaling rule.  Reading: Q, K and V are stored in the OCP 8-bit float E4M3
+  (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no
+  infinities, S.1111.111 is NaN; largest finite 448), each tensor with one
+  positive descale factor: the value of a stored code c is decode(c) times
+  that factor.  What is computed is exact attention of those values; the
+  output is bfloat16.
 * Block-sparse attention: the page writes softmax(S o 1_M) with masked
   entries set to 0, but its algorithm skips the zero blocks, so they carry no
   weight at all.  Reading: masked entries are excluded (-inf), as for the
@@ -115,6 +122,9 @@ __all__ = [
     "forward_dropout_head",
     "backward_dropout_head",
     "finite_difference_grads_dropout",
+    "e4m3_decode",
+    "forward_fp8_head",
+    "fp8_p_rounding_bound",
 ]
 
 
@@ -697,3 +707,61 @@ def finite_difference_grads_dropout(q, k, v, g, keep, t: int, causal: bool = Fal
             gx[idx] = (up - dn) / (2.0 * h)
         grads.append(gx)
     return tuple(grads)
+
+
+# --- FP8 (OCP E4M3) inputs -------------------------------------------------
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of OCP E4M3 codes (uint8 array) as float64.
+
+    Bit 7 is the sign, bits 6..3 the exponent e (bias 7), bits 2..0 the
+    mantissa m: e > 0 gives (1 + m/8) 2^(e - 7), e = 0 the subnormal
+    (m/8) 2^(-6); exponent and mantissa all ones (0x7F, 0xFF) is NaN.  There
+    are no infinities, so the largest finite magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e > 0, (1.0 + m / 8.0) * np.exp2(e - 7.0), (m / 8.0) * 2.0 ** -6)
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def forward_fp8_head(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float,
+                     causal: bool = False, scale: Optional[float] = None):
+    """Attention of E4M3-stored inputs, one head: (O, lse) of the decoded,
+    descaled Q, K, V by the definition of :func:`forward_head`."""
+    q = e4m3_decode(q8) * q_descale
+    k = e4m3_decode(k8) * k_descale
+    v = e4m3_decode(v8) * v_descale
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    return forward_head(q, k, v, causal, scale)
+
+
+def fp8_p_rounding_bound(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float,
+                         causal: bool = False, scale: Optional[float] = None, lazy: float = 2.0 ** 8):
+    """Elementwise bound [N, d] on |O_computed - O| when the probabilities are
+    rounded to E4M3 before they multiply V (the scores, l and the products
+    themselves exact up to fp32).
+
+    A probability is rounded as p' = e^(s - c) for some shift c with
+    m - ln(lazy) <= c <= m (m the row max; lazy >= 1 the largest factor by
+    which p' may exceed 1) and then divided by the normaliser, which is at
+    least sum_j e^(s_j - m).  Rounding to nearest E4M3 errs by at most 2^-4 of
+    p' where p' >= 2^-6 (normal numbers, 3 mantissa bits) and by at most
+    min(p', 2^-10) below (subnormal spacing 2^-9).  Hence
+      |dO_ic| <= sum_j [2^-4 P_ij + min(2^-10, lazy e^(s_ij - m_i)) / L_i] |v_jc|,
+    with P the exact probabilities and L_i = sum_j e^(s_ij - m_i).
+    """
+    q = e4m3_decode(q8) * q_descale
+    k = e4m3_decode(k8) * k_descale
+    v = np.abs(e4m3_decode(v8) * v_descale)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    s = scores(q, k, scale, causal)
+    p, m, l = softmax_stats(s)
+    f = np.exp(s - m[:, None])                     # e^(s - m); 0 where masked
+    sub = np.minimum(2.0 ** -10, lazy * f) / l[:, None]
+    return (2.0 ** -4 * p + sub) @ v

@@ -687,3 +687,64 @@ def test_dropout_pins_catch_an_unmasked_dp():
     dp_wrong = do @ v.T                                  # mistake: no keep mask, no 1/(1 - p)
     ds = p * (dp_wrong - np.sum(p * dp_wrong, axis=-1)[:, None])
     assert np.max(np.abs(0.5 * ds @ k - tq.grad.numpy())) > 1e-3
+
+
+# --- FP8 (OCP E4M3) inputs --------------------------------------------------
+
+def test_e4m3_decode_matches_torch_float8_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = ref.e4m3_decode(codes)
+    theirs = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(theirs))
+    ok = ~np.isnan(mine)
+    assert np.array_equal(mine[ok], theirs[ok])
+
+
+def test_e4m3_decode_special_values():
+    # values fixed by the format: largest finite, smallest normal and subnormal, one, sign
+    assert ref.e4m3_decode(0x7E) == 448.0
+    assert ref.e4m3_decode(0x08) == 2.0 ** -6
+    assert ref.e4m3_decode(0x01) == 2.0 ** -9
+    assert ref.e4m3_decode(0x38) == 1.0
+    assert ref.e4m3_decode(0xB8) == -1.0
+    assert ref.e4m3_decode(0x00) == 0.0 and np.signbit(ref.e4m3_decode(0x80))
+    assert np.isnan(ref.e4m3_decode(0x7F)) and np.isnan(ref.e4m3_decode(0xFF))
+    # 127 distinct finite non-negative values, strictly increasing with the code
+    pos = ref.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)
+
+
+def _fp8_codes(shape, seed, mult=1.0):
+    x = torch.from_numpy(_rand(shape, seed, mult)).float()
+    return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_fp8_is_attention_of_the_decoded_inputs(causal):
+    n, d = 20, 16
+    q8, k8, v8 = (_fp8_codes((n, d), s) for s in (51, 52, 53))
+    o, lse = ref.forward_fp8_head(q8, k8, v8, 0.5, 2.0, 0.25, causal, 0.3)
+    tq = torch.from_numpy(q8).view(torch.float8_e4m3fn).double() * 0.5
+    tk = torch.from_numpy(k8).view(torch.float8_e4m3fn).double() * 2.0
+    tv = torch.from_numpy(v8).view(torch.float8_e4m3fn).double() * 0.25
+    o_t = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.3)
+    np.testing.assert_allclose(o, o_t.numpy(), rtol=0, atol=1e-13)
+
+
+def test_fp8_rounding_bound_holds_for_probabilities_rounded_to_e4m3():
+    # emulate the rounding the bound describes (p' = e^(s - c) rounded to E4M3, c = m or m - ln 256)
+    n, d = 48, 32
+    q8, k8, v8 = (_fp8_codes((n, d), s, 1.5) for s in (61, 62, 63))
+    q, k, v = (ref.e4m3_decode(x) for x in (q8, k8, v8))
+    s = ref.scores(q, k, 0.4, True)
+    m = np.max(s, axis=-1)
+    o_exact, _ = ref.forward_head(q, k, v, True, 0.4)
+    bound = ref.fp8_p_rounding_bound(q8, k8, v8, 1.0, 1.0, 1.0, True, 0.4)
+    for shift in (0.0, math.log(256.0)):
+        pp = np.exp(s - (m - shift)[:, None])
+        pq = torch.from_numpy(pp).float().to(torch.float8_e4m3fn).double().numpy()
+        l = np.sum(pp, axis=-1)
+        o_rounded = (pq @ v) / l[:, None]
+        err = np.abs(o_rounded - o_exact)
+        assert np.all(err <= bound + 1e-12)
+        assert err.max() > 0.01 * bound.max()        # the bound is not vacuous
