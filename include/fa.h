@@ -61,7 +61,7 @@ enum fa_status {
   FA_ERR_SHAPE = 2,     /* B, H or N negative, or one head's N*d elements exceed 2^31 - 1 bytes */
   FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 */
   FA_ERR_DTYPE = 4,     /* dtype is not an fa_dtype */
-  FA_ERR_SCALE = 5,     /* scale is NaN, infinite or negative */
+  FA_ERR_SCALE = 5,     /* scale is NaN, infinite or negative (FP8 descale factors: not finite or <= 0) */
   FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than fa_backward_workspace_size */
   FA_ERR_HIP = 7,       /* the HIP runtime reported an error at launch */
   FA_ERR_ALIGN = 8,     /* a tensor pointer is not 16-byte aligned */
@@ -155,6 +155,25 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
                 int B, int H, int N, int d, int causal, float scale, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Forward with 8-bit float inputs.  q, k, v: [B,H,N,d] in the OCP FP8 format
+ * E4M3 (one byte per element: sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, subnormals, no infinities, largest finite 448), each tensor with one
+ * descale factor: an element's value is its stored number times the factor
+ * (finite and > 0, else FA_ERR_SCALE).  Computes
+ *   O = softmax(scale * (q_descale Q)(k_descale K)^T) (v_descale V)
+ * with O written in bfloat16 [B,H,N,d] and lse [B,H,N] float32 as in
+ * fa_forward.  Both products run on the 8-bit matrix core (fp32
+ * accumulation); the probabilities are rounded to E4M3 (nearest even) before
+ * they multiply V, while the row sums use them unrounded.  FP8 is named on
+ * "Как работает FlashAttention математически", section 9 (FlashAttention-3),
+ * without a format; format and scaling are this library's.  Everything else
+ * as fa_forward.
+ */
+int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, int causal, float scale,
+                   float q_descale, float k_descale, float v_descale, void* stream);
 
 /*
  * Attention with dropout on the probabilities, forward and backward

@@ -19,12 +19,12 @@ from . import _lib
 from ._lib import (FA_BF16, FA_F32, FaError, fa_backward, fa_backward_dkdv, fa_backward_dq, fa_backward_dropout,
                    fa_backward_preprocess, fa_backward_workspace_size, fa_decode, fa_decode_num_splits,
                    fa_decode_workspace_size, fa_forward, fa_forward_block_sparse, fa_forward_dropout,
-                   fa_strerror)
+                   fa_forward_fp8, fa_strerror)
 
-__all__ = ["forward", "forward_block_sparse", "backward", "decode", "workspace_size", "FaError", "FA_F32",
+__all__ = ["forward", "forward_block_sparse", "forward_fp8", "backward", "decode", "workspace_size", "FaError", "FA_F32",
            "FA_BF16", "fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_size",
            "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_forward_dropout",
-           "fa_backward_dropout", "fa_decode",
+           "fa_backward_dropout", "fa_forward_fp8", "fa_decode",
            "fa_decode_workspace_size", "fa_decode_num_splits", "fa_strerror", "load_library",
            "backward_stages"]
 
@@ -94,6 +94,38 @@ def forward(q, k, v, causal: bool = False, scale: Optional[float] = None,
                     B, H, N, d, causal, scale, _dtype_code(q), _stream_ptr(q.device))
     if st != 0:
         raise FaError(st, "fa_forward")
+    return out, lse
+
+
+def forward_fp8(q, k, v, causal: bool = False, scale: Optional[float] = None, q_descale: float = 1.0,
+                k_descale: float = 1.0, v_descale: float = 1.0, out=None, lse=None):
+    """Attention of FP8 (OCP E4M3) inputs with per-tensor descale factors.
+
+    q, k, v: [B, H, N, d] tensors of dtype torch.float8_e4m3fn (or uint8 holding
+    the codes); O is returned in bfloat16, lse in float32.
+    """
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if q.device.type != "cuda":
+        raise ValueError("tensors must live on a ROCm device")
+    if q.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise TypeError("q, k, v must be torch.float8_e4m3fn (or uint8 codes)")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(name, t, q.shape, q.dtype, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check("out", out, (B, H, N, d), torch.bfloat16, q.device)
+    _check("lse", lse, (B, H, N), torch.float32, q.device)
+    st = fa_forward_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                        causal, scale, q_descale, k_descale, v_descale, _stream_ptr(q.device))
+    if st != 0:
+        raise FaError(st, "fa_forward_fp8")
     return out, lse
 
 

@@ -22,7 +22,7 @@ STATUS = {
 }
 EXPORTED = ("fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_size",
             "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_forward_dropout",
-            "fa_backward_dropout", "fa_decode",
+            "fa_backward_dropout", "fa_forward_fp8", "fa_decode",
             "fa_decode_workspace_size", "fa_decode_num_splits", "fa_strerror")
 
 _lock = threading.Lock()
@@ -69,6 +69,8 @@ def load() -> ctypes.CDLL:
         lib.fa_backward_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, f, u64, u32,
                                             vp, sz, vp]
         lib.fa_backward_dropout.restype = i
+        lib.fa_forward_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, f, f, f, vp]
+        lib.fa_forward_fp8.restype = i
         lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
         lib.fa_decode.restype = i
         lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i]
@@ -127,6 +129,11 @@ def fa_backward_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, s
     return load().fa_backward_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, int(causal), float(scale),
                                       dtype, float(p_drop), int(seed), int(offset), workspace, workspace_bytes,
                                       stream)
+
+
+def fa_forward_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, q_descale, k_descale, v_descale, stream) -> int:
+    return load().fa_forward_fp8(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), float(q_descale),
+                                 float(k_descale), float(v_descale), stream)
 
 
 def fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, num_splits,

@@ -122,6 +122,22 @@ int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, flo
   return hip_status(fa::launch_forward(a, static_cast<hipStream_t>(stream)));
 }
 
+int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   int causal, float scale, float q_descale, float k_descale, float v_descale, void* stream) {
+  bool empty = false;
+  // bf16 output: the per-head size check of the bf16 layout covers the one-byte inputs too
+  const int st = check_shape(B, H, N, d, FA_BF16, scale, &empty);
+  if (st != FA_OK) return st;
+  const float ds[] = {q_descale, k_descale, v_descale};
+  for (float x : ds)
+    if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_SCALE;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  fa::Fp8Args a{q, k, v, o, lse, B, H, N, d, causal ? 1 : 0, scale, q_descale, k_descale, v_descale};
+  return hip_status(fa::launch_forward_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
 int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
                             const unsigned char* block_mask, int mask_heads, int block_q, int block_k, int B,
                             int H, int N, int d, int causal, float scale, int dtype, void* stream) {
@@ -253,7 +269,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_SHAPE: return "invalid shape: B, H or N negative, or the problem is too large";
     case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
     case FA_ERR_DTYPE: return "unsupported dtype: use FA_F32 or FA_BF16";
-    case FA_ERR_SCALE: return "invalid scale: must be finite and >= 0";
+    case FA_ERR_SCALE: return "invalid scale: must be finite and >= 0 (FP8 descale factors: finite and > 0)";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_backward_workspace_size()";
     case FA_ERR_HIP: return "the HIP runtime reported an error at launch";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned (workspace: 256-byte)";

@@ -52,6 +52,17 @@ struct BwdArgs {
   DropParams drop{};
 };
 
+// Forward with OCP E4M3 inputs (one byte per element) and bf16 output.
+struct Fp8Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;          // bf16 [B, H, N, d]
+  float* lse;
+  int B, H, N, d, causal;
+  float scale, q_descale, k_descale, v_descale;
+};
+
 struct DecArgs {
   const void* q;     // [B, H, Nq, d]
   const void* k;     // [B, H, Nk, d]
@@ -92,6 +103,7 @@ inline size_t ws_bytes(size_t rows) { return 2 * ws_dsum_bytes(rows); }
 
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecArgs& a, hipStream_t stream);
+hipError_t launch_forward_fp8(const Fp8Args& a, hipStream_t stream);
 // backward stages (bit mask; 7 = all): D, then dK/dV, then dQ
 constexpr int kStagePre = 1, kStageDkDv = 2, kStageDq = 4;
 hipError_t launch_backward(const BwdArgs& a, int stages, hipStream_t stream);

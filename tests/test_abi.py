@@ -20,7 +20,7 @@ FAKE = 0x1000  # 16-byte aligned, never dereferenced: validation fails first
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -290,3 +290,25 @@ def test_dropout_empty_problem_is_a_noop_but_checks_p():
     assert fwd_drop(N=0, q=0) == 0
     assert bwd_drop(B=0, q=0) == 0
     assert fwd_drop(N=0, p=2.0) == 10
+
+
+def fwd_fp8(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, N=64, d=128, causal=1, scale=0.1,
+             qs=1.0, ks=0.5, vs=2.0, stream=None)
+    a.update(kw)
+    return fa.fa_forward_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["causal"],
+                             a["scale"], a["qs"], a["ks"], a["vs"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), 1), (dict(o=0), 1), (dict(N=-1), 2), (dict(N=1 << 23, q=0), 2), (dict(d=96), 3),
+    (dict(scale=float("nan")), 5), (dict(qs=0.0), 5), (dict(ks=-1.0), 5), (dict(vs=float("inf")), 5),
+    (dict(v=FAKE + 8), 8), (dict(N=1 << 22, q=0), 1),
+])
+def test_forward_fp8_rejects_invalid_arguments(kw, status):
+    assert fwd_fp8(**kw) == status
+
+
+def test_forward_fp8_empty_problem_is_a_noop():
+    assert fwd_fp8(N=0, q=0) == 0
+    assert fwd_fp8(N=0, qs=0.0) == 5

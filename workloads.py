@@ -142,3 +142,15 @@ def decode_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, seed: in
     v = torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32) * mult
     td = torch.float32 if dtype == "f32" else torch.bfloat16
     return {name: t.to(td).contiguous() for name, t in (("q", q), ("k", k), ("v", v))}
+
+
+def fp8_inputs(B: int, H: int, N: int, d: int, seed: int, mult: float = 1.0):
+    """Seeded N(0,1)*mult q, k, v rounded once to OCP E4M3 (torch.float8_e4m3fn),
+    returned as uint8 codes [B, H, N, d] (CPU tensors)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    out = {}
+    for name in ("q", "k", "v"):
+        x = torch.randn((B, H, N, d), generator=g, dtype=torch.float32) * mult
+        out[name] = x.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    return out
