@@ -12,7 +12,8 @@ FLOP counting convention: forward 4*B*H*N^2*d, halved when causal; backward
 the wall time of a step, in TFLOP/s.
 
 Prints ONE JSON line.  Options: --gpus N (only 1: the path runs on one GPU),
---steps K, --warmup W, --no-cpu-baseline, --no-extra, --decode-only, --dropout-only.
+--steps K, --warmup W, --no-cpu-baseline, --no-extra, --decode-only, --dropout-only,
+--fp8-only.
 """
 from __future__ import annotations
 
@@ -296,6 +297,53 @@ def dropout_measurement(fa, torch, dev, steps, p_drop=0.1):
     return res
 
 
+PEAK_FP8_TFLOPS = 5000.0     # MI355X published dense fp8 MFMA peak
+
+
+def fp8_measurement(fa, torch, dev, steps):
+    """Forward with OCP E4M3 inputs on the 16K causal d=128 shape (the bench
+    recipe rounded to E4M3), against the bf16 forward on the same values.
+    FLOPs by the forward convention; peak = the published dense fp8 rate."""
+    from workloads import PROBLEMS, make_inputs
+    p = PROBLEMS["causal_16k_d128"]
+    inputs = make_inputs(p)
+    q16, k16, v16 = (inputs[n].to(dev) for n in ("q", "k", "v"))
+    del inputs
+    q8, k8, v8 = (t.float().to(torch.float8_e4m3fn) for t in (q16, k16, v16))
+    o = torch.empty_like(q16)
+    lse = torch.empty((p.B, p.H, p.N), dtype=torch.float32, device=dev)
+    raw = fa.load_library()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run8():
+        st = raw.fa_forward_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(), p.B, p.H,
+                                p.N, p.d, 1, p.scale, 1.0, 1.0, 1.0, stream)
+        assert st == 0, st
+
+    def run16():
+        st = raw.fa_forward(q16.data_ptr(), k16.data_ptr(), v16.data_ptr(), o.data_ptr(), lse.data_ptr(), p.B, p.H,
+                            p.N, p.d, 1, p.scale, 1, stream)
+        assert st == 0, st
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms8, ms16 = timed(run8), timed(run16)
+    flops = p.fwd_flops()
+    return {"workload": f"{p.name} forward, Q/K/V rounded to OCP E4M3 (descale 1), bf16 output",
+            "ms": ms8, "tflops": flops / ms8 * 1e-9, "frac_fp8_peak": flops / ms8 * 1e-9 / PEAK_FP8_TFLOPS,
+            "bf16_forward_ms": ms16, "speedup_vs_bf16": ms16 / ms8}
+
+
 DECODE_SHAPES = [(1, 32, 1, 65536), (8, 32, 1, 8192)]    # (B, H, Nq, Nk), d = 128, bf16, causal
 
 
@@ -384,9 +432,11 @@ def main(argv=None):
     ap.add_argument("--cpu-heads", type=int, default=4, help="whole heads timed on the CPU oracle")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the side measurements (N=4K d=128 fwd+bwd, block-sparse 16K forward, "
-                         "split-KV decoding, dropout)")
+                         "split-KV decoding, dropout, FP8 forward)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the split-KV decoding measurement (one JSON line; for kernel traces)")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="only the FP8 forward measurement (one JSON line; for kernel traces)")
     ap.add_argument("--dropout-only", action="store_true",
                     help="only the dropout measurement (one JSON line; for kernel traces)")
     ap.add_argument("--decode-shape", type=int, default=None,
@@ -420,6 +470,9 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": {"bytes_read_per_copy": 4 * n, "bytes_written_per_copy": 4 * n,
                                                "copies": 3}}), flush=True)
+        return 0
+    if args.fp8_only:
+        print(json.dumps({"fp8_16k_d128": fp8_measurement(fa, torch, dev, max(3, args.steps))}), flush=True)
         return 0
     if args.dropout_only:
         print(json.dumps({"dropout_16k_d128": dropout_measurement(fa, torch, dev, max(3, args.steps))}), flush=True)
@@ -461,6 +514,8 @@ def main(argv=None):
         extra["decode_bf16_d128"] = decode_measurement(fa, torch, dev, max(10, args.steps))
         torch.cuda.empty_cache()
         extra["dropout_16k_d128"] = dropout_measurement(fa, torch, dev, max(5, args.steps // 2))
+        torch.cuda.empty_cache()
+        extra["fp8_16k_d128"] = fp8_measurement(fa, torch, dev, max(5, args.steps // 2))
 
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
