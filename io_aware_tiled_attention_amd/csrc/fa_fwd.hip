@@ -14,15 +14,16 @@
 //     sweep over keys;
 //   * K and V stream through LDS in tiles of BC = 64 keys, global -> LDS
 //     directly (buffer_load ... lds), two stages deep: while tile j is being
-//     consumed, K of tile j+2 and V of tile j+1 are in flight;
+//     consumed, K and V of tile j+1 are in flight;
 //   * per tile each wave computes S^T = K_j Q_i^T on the matrix cores, so
 //     that each lane holds 32 scores of ONE query: the row max needs only an
 //     in-lane reduction and one exchange with the partner lane l^32
 //     (v_permlane32_swap), and the rescale of O by exp(m_old - m_new) is one
 //     per-lane scalar;
-//   * software pipelining inside the wave: the products S_{j+1} are issued
-//     before the softmax of tile j, so the matrix core works on them while the
-//     vector unit does the exponentials of tile j;
+//   * a wave's matrix and vector work do not overlap each other (measured),
+//     so S of a tile is computed right before its softmax; overlap comes from
+//     the other wave on the SIMD.  (Issuing S of the next tile before the
+//     softmax only cost 32 registers and ~2%.)
 //   * the online-softmax update ("FlashAttention in NeurIPS 2022" section 2.1;
 //     "Как работает FlashAttention математически" sections 3-4) keeps O
 //     un-normalised and divides by l once at the end; the shift inside the
@@ -203,30 +204,24 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 
   // Prologue: K and V of the first visited tile (and K of the second)
   // resident; its S computed.
-  f32x16 s_cur[NKB], s_nxt[NKB];
+  f32x16 s_cur[NKB];
   if (n_act > 0) {
     tile_to_lds<T, D, kFwdBC, kFwdWaves>(rk, L::k(smem, 0), tile_of(0) * kFwdBC, w, lane);
     tile_to_lds<T, D, kFwdBC, kFwdWaves>(rv, L::v(smem, 0), tile_of(0) * kFwdBC, w, lane);
-    if (n_act > 1) tile_to_lds<T, D, kFwdBC, kFwdWaves>(rk, L::k(smem, 1), tile_of(1) * kFwdBC, w, lane);
     wait_vmem();
-    __syncthreads();
-    if (active(0)) compute_st(s_cur, L::k(smem, 0));
-    // iteration 0 refills K stage 0 (with the third tile): every wave must
-    // have read the first tile's K fragments first
     __syncthreads();
   }
 
   for (int it = 0; it < n_act; ++it) {
     const int j = tile_of(it);
     const int kv0 = j * kFwdBC;
-    if (it + 2 < n_act)
-      tile_to_lds<T, D, kFwdBC, kFwdWaves>(rk, L::k(smem, it & 1), tile_of(it + 2) * kFwdBC, w, lane);
-    if (it + 1 < n_act)
+    if (it + 1 < n_act) {
+      tile_to_lds<T, D, kFwdBC, kFwdWaves>(rk, L::k(smem, (it + 1) & 1), tile_of(it + 1) * kFwdBC, w, lane);
       tile_to_lds<T, D, kFwdBC, kFwdWaves>(rv, L::v(smem, (it + 1) & 1), tile_of(it + 1) * kFwdBC, w, lane);
-    // S of the next tile goes to the matrix core first; the vector work below overlaps it.
-    if (it + 1 < n_act && active(it + 1)) compute_st(s_nxt, L::k(smem, (it + 1) & 1));
+    }
 
     if (active(it)) {
+      compute_st(s_cur, L::k(smem, it & 1));
       const bool masked = (CAUSAL && kv0 + kFwdBC - 1 > qw0) || (kv0 + kFwdBC > N);
       if (masked) {
         // keys allowed for this lane: key <= min(N-1, myq) (causal) or key <= N-1
@@ -302,8 +297,6 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 
     wait_vmem();
     __syncthreads();
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s_cur[kb] = s_nxt[kb];
   }
 
   // Epilogue: O = O_acc / l (deferred normalisation), lse = shift + ln l;

@@ -25,7 +25,10 @@
 //     2e + i/8 (e = 0..7) -- 8 consecutive keys of one d column;
 //   * l sums the unrounded probabilities, so only P's rounding enters O.
 // K/V tiles are 64 keys x D bytes, swizzled so that both the 16-byte K reads
-// and the transpose reads are free of bank conflicts.
+// and the transpose reads are free of bank conflicts.  S of a tile is
+// computed right before its softmax (no second set of S registers), which
+// leaves room for three waves per SIMD: the vector work of one wave then
+// overlaps the matrix work of another more often.
 #include <algorithm>
 
 #include "fa_common.h"
@@ -94,7 +97,7 @@ __device__ __forceinline__ int pack4_e4m3(float a, float b, float c, float d) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kF8Threads, 2)
+__global__ __launch_bounds__(kF8Threads, 3)
 void fa_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned char* __restrict__ K,
                        const unsigned char* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE, int N,
                        int BH, int n_qtiles, float kfac, float v_descale) {
@@ -176,23 +179,21 @@ void fa_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned char*
   float msub = kNegInf;   // exponent shift (running max of scaled scores, raised lazily)
   float l_run = 0.f;      // this lane's share of the running row sum, relative to msub
 
-  f32x16 s_cur[NKB], s_nxt[NKB];
+  f32x16 s_cur[NKB];
   tile8_to_lds<D>(rk, L::k(smem, 0), 0, w, lane);
   tile8_to_lds<D>(rv, L::v(smem, 0), 0, w, lane);
-  if (ntiles > 1) tile8_to_lds<D>(rk, L::k(smem, 1), kF8BC, w, lane);
   wait_vmem();
-  __syncthreads();
-  compute_st(s_cur, L::k(smem, 0));
-  // iteration 0 refills K stage 0: every wave must have read the first tile's K first
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     const int kv0 = it * kF8BC;
-    if (it + 2 < ntiles) tile8_to_lds<D>(rk, L::k(smem, it & 1), (it + 2) * kF8BC, w, lane);
-    if (it + 1 < ntiles) tile8_to_lds<D>(rv, L::v(smem, (it + 1) & 1), (it + 1) * kF8BC, w, lane);
-    if (it + 1 <= wave_last) compute_st(s_nxt, L::k(smem, (it + 1) & 1));
+    if (it + 1 < ntiles) {
+      tile8_to_lds<D>(rk, L::k(smem, (it + 1) & 1), (it + 1) * kF8BC, w, lane);
+      tile8_to_lds<D>(rv, L::v(smem, (it + 1) & 1), (it + 1) * kF8BC, w, lane);
+    }
 
     if (it <= wave_last) {
+      compute_st(s_cur, L::k(smem, it & 1));
       const bool masked = (CAUSAL && kv0 + kF8BC - 1 > qw0) || (kv0 + kF8BC > N);
       if (masked) {
         const int last = CAUSAL ? min(N - 1, myq) : N - 1;   // keys allowed: key <= last
@@ -263,8 +264,6 @@ void fa_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned char*
 
     wait_vmem();
     __syncthreads();
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s_cur[kb] = s_nxt[kb];
   }
 
   // O = v_descale * O_acc / l, lse = shift + ln l (natural log units).
