@@ -11,6 +11,11 @@ FLOP counting convention: forward 4*B*H*N^2*d, halved when causal; backward
 2.5x forward.  The value is total (forward + backward) FLOPs per step over
 the wall time of a step, in TFLOP/s.
 
+Besides the step, "extra" carries the 4K shape, the block-sparse, decoding,
+dropout and FP8 paths, and the library GEMM's rate on N(0,1) operands in the
+same run (the practical matrix-core ceiling for such data, with each kernel's
+fraction of it).
+
 Prints ONE JSON line.  Options: --gpus N (only 1: the path runs on one GPU),
 --steps K, --warmup W, --no-cpu-baseline, --no-extra, --decode-only, --dropout-only,
 --fp8-only.
@@ -344,6 +349,52 @@ def fp8_measurement(fa, torch, dev, steps):
             "bf16_forward_ms": ms16, "speedup_vs_bf16": ms16 / ms8}
 
 
+def gemm_ceiling_measurement(torch, dev, steps, n=16384):
+    """The practical matrix-core ceiling on this chip for data like the bench's:
+    the vendor library's dense GEMM (torch.matmul -> hipBLASLt, bf16; and
+    torch._scaled_mm, OCP E4M3 with bf16 output) on n x n x n operands drawn
+    N(0,1).  The power manager lowers the clock with the data paths' switching
+    activity, so random operands run well below the published peak; this is
+    the rate the attention kernels' fractions are best read against.  Context
+    only: the attention path does not call these routines."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(7)
+    a = torch.randn((n, n), generator=g, dtype=torch.float32)
+    b = torch.randn((n, n), generator=g, dtype=torch.float32)
+    a16, b16 = a.to(torch.bfloat16).to(dev), b.to(torch.bfloat16).to(dev)
+    del a, b
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    flops = 2.0 * n * n * n
+    out = {"what": f"library GEMM {n}x{n}x{n} on N(0,1) operands (torch.matmul bf16; torch._scaled_mm E4M3 -> bf16)"}
+    ms = timed(lambda: torch.matmul(a16, b16))
+    out["bf16_tflops"] = flops / ms * 1e-9
+    out["bf16_frac_peak"] = out["bf16_tflops"] / PEAK_BF16_TFLOPS
+    try:
+        one = torch.ones((), dtype=torch.float32, device=dev)
+        a8 = a16.float().to(torch.float8_e4m3fn)
+        b8 = b16.float().to(torch.float8_e4m3fn).t().contiguous().t()   # column-major right operand
+        ms8 = timed(lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one, out_dtype=torch.bfloat16))
+        out["fp8_tflops"] = flops / ms8 * 1e-9
+        out["fp8_frac_peak"] = out["fp8_tflops"] / PEAK_FP8_TFLOPS
+        del a8, b8
+    except Exception as e:   # an FP8 GEMM this torch build lacks is reported, not fatal
+        out["fp8_error"] = f"{type(e).__name__}: {e}"[:200]
+    del a16, b16
+    return out
+
+
 DECODE_SHAPES = [(1, 32, 1, 65536), (8, 32, 1, 8192)]    # (B, H, Nq, Nk), d = 128, bf16, causal
 
 
@@ -516,6 +567,15 @@ def main(argv=None):
         extra["dropout_16k_d128"] = dropout_measurement(fa, torch, dev, max(5, args.steps // 2))
         torch.cuda.empty_cache()
         extra["fp8_16k_d128"] = fp8_measurement(fa, torch, dev, max(5, args.steps // 2))
+        torch.cuda.empty_cache()
+        ceil = gemm_ceiling_measurement(torch, dev, 5)
+        g16 = ceil["bf16_tflops"]
+        ceil["frac_of_bf16_gemm"] = {"fwd": kt["fwd"]["tflops"] / g16, "bwd_dkdv": kt["bwd_dkdv"]["tflops"] / g16,
+                                     "bwd_dq": kt["bwd_dq"]["tflops"] / g16,
+                                     "bwd_total": kt["bwd_total"]["tflops"] / g16}
+        if "fp8_tflops" in ceil:
+            ceil["fp8_fwd_frac_of_fp8_gemm"] = extra["fp8_16k_d128"]["tflops"] / ceil["fp8_tflops"]
+        extra["gemm_ceiling"] = ceil
 
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -96,7 +96,8 @@ template <typename T, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kBwdThreads, 2)
 void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                         const T* __restrict__ dO, const float* __restrict__ dsum, const float* __restrict__ nlse,
-                        T* __restrict__ dK, T* __restrict__ dV, int N, int BH, float scale, DropParams dpar) {
+                        T* __restrict__ dK, T* __restrict__ dV, int N, int BH, int n_ktiles, int group, float scale,
+                        DropParams dpar) {
   using M = Mfma<T>;
   using C = BwdCfg<T, D>;
   using G = Tile<T, D>;                 // Q and dO tiles: BQ rows x D
@@ -114,8 +115,10 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
   const int g = lane >> 5;
   const int r32 = lane & 31;
 
-  const int bh = blockIdx.x % BH;
-  const int kt = blockIdx.x / BH;             // causal: low key tiles (most work) first
+  // heads grouped per XCD; causal: low key tiles (most work) first
+  const WgOrder wo = wg_order(blockIdx.x, BH, n_ktiles, group);
+  const int bh = wo.bh;
+  const int kt = wo.rank;
   const int k0 = kt * kBwdBK;
   const int kw0 = k0 + w * kBwdKW;
   const int mykey = kw0 + r32;
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(kKvThreads, 1)
 void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                              const bf16* __restrict__ dO, const float* __restrict__ dsum,
                              const float* __restrict__ nlse, bf16* __restrict__ dK, bf16* __restrict__ dV, int N,
-                             int BH, float scale, DropParams dpar) {
+                             int BH, int n_ktiles, int group, float scale, DropParams dpar) {
   using M = Mfma<bf16>;
   using C = KvCfg<D>;
   using G = Tile<bf16, D>;
@@ -346,8 +349,10 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
   const int g = lane >> 5;
   const int r32 = lane & 31;
 
-  const int bh = blockIdx.x % BH;
-  const int kt = blockIdx.x / BH;             // causal: low key tiles (most work) first
+  // heads grouped per XCD; causal: low key tiles (most work) first
+  const WgOrder wo = wg_order(blockIdx.x, BH, n_ktiles, group);
+  const int bh = wo.bh;
+  const int kt = wo.rank;
   const int k0 = kt * kBwdBK;
   const int kw0 = k0 + slice * kBwdKW;
   const int mykey = kw0 + r32;
@@ -581,7 +586,7 @@ template <typename T, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kDqThreads, sizeof(T) == 2 ? 2 : 1)
 void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                       const T* __restrict__ dO, const float* __restrict__ dsum, const float* __restrict__ nlse,
-                      T* __restrict__ dQ, int N, int BH, int n_qtiles, float scale, DropParams dpar) {
+                      T* __restrict__ dQ, int N, int BH, int n_qtiles, int group, float scale, DropParams dpar) {
   using M = Mfma<T>;
   using G = Tile<T, D>;
   using X = ExpDomain<T>;
@@ -599,9 +604,10 @@ void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
   const int g = lane >> 5;
   const int r32 = lane & 31;
 
-  const int bh = blockIdx.x % BH;
-  int qt = blockIdx.x / BH;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;         // longest first
+  // heads grouped per XCD; causal: longest first
+  const WgOrder wo = wg_order(blockIdx.x, BH, n_qtiles, group);
+  const int bh = wo.bh;
+  const int qt = CAUSAL ? n_qtiles - 1 - wo.rank : wo.rank;
   const int q0 = qt * kDqBR;
   const size_t head = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * G::R;
@@ -734,7 +740,7 @@ __global__ __launch_bounds__(kDqThreads, 2)
 void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                            const bf16* __restrict__ dO, const float* __restrict__ dsum,
                            const float* __restrict__ nlse, bf16* __restrict__ dQ, int N, int BH, int n_qtiles,
-                           float scale, DropParams dpar) {
+                           int group, float scale, DropParams dpar) {
   using M = Mfma<bf16>;
   using G = Tile<bf16, D>;
   using X = ExpDomain<bf16>;
@@ -754,9 +760,10 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   const int g = lane >> 5;
   const int r32 = lane & 31;
 
-  const int bh = blockIdx.x % BH;
-  int qt = blockIdx.x / BH;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;         // longest first
+  // heads grouped per XCD; causal: longest first
+  const WgOrder wo = wg_order(blockIdx.x, BH, n_qtiles, group);
+  const int bh = wo.bh;
+  const int qt = CAUSAL ? n_qtiles - 1 - wo.rank : wo.rank;
   const int q0 = qt * kDqBR;
   const size_t head = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * G::R;
@@ -956,7 +963,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
       hipLaunchKernelGGL((fa_bwd_dkdv_bf16_kernel<D, CAUSAL, DROP>), dim3(n_ktiles * BH), dim3(kKvThreads), 0,
                          stream, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                          static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.dsum, a.nlse,
-                         static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, BH, a.scale, a.drop);
+                         static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, BH, n_ktiles,
+                         wg_group(n_ktiles, 32), a.scale, a.drop);   // 1 workgroup per CU
     } else {
       using C = BwdCfg<T, D>;
       auto kern = fa_bwd_dkdv_kernel<T, D, CAUSAL, DROP>;
@@ -966,7 +974,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
       hipLaunchKernelGGL(kern, dim3(n_ktiles * BH), dim3(kBwdThreads), C::BYTES, stream,
                          static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                          static_cast<const T*>(a.dout), a.dsum, a.nlse, static_cast<T*>(a.dk),
-                         static_cast<T*>(a.dv), a.N, BH, a.scale, a.drop);
+                         static_cast<T*>(a.dv), a.N, BH, n_ktiles, wg_group(n_ktiles, 32), a.scale, a.drop);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -976,7 +984,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
       hipLaunchKernelGGL((fa_bwd_dq_bf16_kernel<D, CAUSAL, DROP>), dim3(n_qtiles * BH), dim3(kDqThreads), 0,
                          stream, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                          static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.dsum, a.nlse,
-                         static_cast<bf16*>(a.dq), a.N, BH, n_qtiles, a.scale, a.drop);
+                         static_cast<bf16*>(a.dq), a.N, BH, n_qtiles,
+                         wg_group(n_qtiles, 64), a.scale, a.drop);   // 2 workgroups per CU
     } else {
       constexpr int bytes = 4 * kDqBC * D * (int)sizeof(T);
       auto kern = fa_bwd_dq_kernel<T, D, CAUSAL, DROP>;
@@ -985,7 +994,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
       if (attr_err != hipSuccess) return attr_err;
       hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(kDqThreads), bytes, stream, static_cast<const T*>(a.q),
                          static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<const T*>(a.dout),
-                         a.dsum, a.nlse, static_cast<T*>(a.dq), a.N, BH, n_qtiles, a.scale, a.drop);
+                         a.dsum, a.nlse, static_cast<T*>(a.dq), a.N, BH, n_qtiles, wg_group(n_qtiles, 32),
+                         a.scale, a.drop);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -80,7 +80,7 @@ struct FwdSmem {
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(kFwdThreads, sizeof(T) == 2 ? 2 : 1)
 void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-                   T* __restrict__ O, float* __restrict__ LSE, int N, int BH, int n_qtiles, float scale,
+                   T* __restrict__ O, float* __restrict__ LSE, int N, int BH, int n_qtiles, int group, float scale,
                    const unsigned char* __restrict__ mask, int H, int mask_heads, int block_q, int block_k,
                    DropParams dp) {
   using M = Mfma<T>;
@@ -100,10 +100,11 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   const int g = lane >> 5;
   const int r32 = lane & 31;
 
-  // Longest-first for causal: the last query tiles see the most keys.
-  const int bh = blockIdx.x % BH;
-  int qt = blockIdx.x / BH;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  // Launch order: heads grouped per XCD, and longest-first for causal (rank
+  // 0 = the last query tile, which sees the most keys).
+  const WgOrder wo = wg_order(blockIdx.x, BH, n_qtiles, group);
+  const int bh = wo.bh;
+  const int qt = CAUSAL ? n_qtiles - 1 - wo.rank : wo.rank;
   const int q0 = qt * kFwdBR;
   const size_t head = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * G::R;
@@ -331,9 +332,11 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int BH = a.B * a.H;
   const int n_qtiles = (a.N + kFwdBR - 1) / kFwdBR;
   const dim3 grid(n_qtiles * BH), block(kFwdThreads);
+  // resident workgroups per XCD: 32 CUs x (2 for bf16, 1 for fp32)
+  const int group = wg_group(n_qtiles, 32 * (sizeof(T) == 2 ? 2 : 1));
   hipLaunchKernelGGL(kern, grid, block, bytes, stream, static_cast<const T*>(a.q),
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<T*>(a.o),
-                     a.lse, a.N, BH, n_qtiles, a.scale, a.mask, a.H, a.mask_heads, a.block_q, a.block_k, a.drop);
+                     a.lse, a.N, BH, n_qtiles, group, a.scale, a.mask, a.H, a.mask_heads, a.block_q, a.block_k, a.drop);
   return hipGetLastError();
 }
 

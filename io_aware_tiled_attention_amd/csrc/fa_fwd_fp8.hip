@@ -100,7 +100,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kF8Threads, 3)
 void fa_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned char* __restrict__ K,
                        const unsigned char* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE, int N,
-                       int BH, int n_qtiles, float kfac, float v_descale) {
+                       int BH, int n_qtiles, int group, float kfac, float v_descale) {
   using L = F8Smem<D>;
   using G = Tile8<D>;
   using X = ExpDomain<bf16>;                   // base-2 exponent domain
@@ -116,9 +116,10 @@ void fa_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned char*
   const int g = lane >> 5;
   const int r32 = lane & 31;
 
-  const int bh = blockIdx.x % BH;
-  int qt = blockIdx.x / BH;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;         // longest first
+  // heads grouped per XCD, longest-first for causal
+  const WgOrder wo = wg_order(blockIdx.x, BH, n_qtiles, group);
+  const int bh = wo.bh;
+  const int qt = CAUSAL ? n_qtiles - 1 - wo.rank : wo.rank;
   const int q0 = qt * kF8BR;
   const size_t head = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * G::R;
@@ -296,8 +297,8 @@ hipError_t launch_fp8_t(const Fp8Args& a, hipStream_t stream) {
   const float kfac = std::max(a.scale * a.q_descale * a.k_descale * kLog2e, kMinFactor);
   hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(kF8Threads), bytes, stream,
                      static_cast<const unsigned char*>(a.q), static_cast<const unsigned char*>(a.k),
-                     static_cast<const unsigned char*>(a.v), static_cast<bf16*>(a.o), a.lse, a.N, BH, n_qtiles, kfac,
-                     a.v_descale);
+                     static_cast<const unsigned char*>(a.v), static_cast<bf16*>(a.o), a.lse, a.N, BH, n_qtiles,
+                     wg_group(n_qtiles, 32 * 3), kfac, a.v_descale);   // 3 workgroups per CU
   return hipGetLastError();
 }
 
