@@ -58,7 +58,7 @@ enum fa_dtype {
 enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,      /* a required pointer is NULL (non-empty problem) */
-  FA_ERR_SHAPE = 2,     /* B, H or N negative, or one head's N*d elements exceed 2^31 - 1 bytes */
+  FA_ERR_SHAPE = 2,     /* B, H or N negative, or one head's (N + 256) * d elements exceed 2^31 - 1 bytes */
   FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 */
   FA_ERR_DTYPE = 4,     /* dtype is not an fa_dtype */
   FA_ERR_SCALE = 5,     /* scale is NaN, infinite or negative (FP8 descale factors: not finite or <= 0) */

@@ -20,10 +20,13 @@ int check_shape(int B, int H, int N, int d, int dtype, float scale, bool* empty)
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
   // Sizes must fit the kernels' index arithmetic: rows and per-head byte
-  // offsets use 32-bit ints, whole-tensor offsets 64-bit.
+  // offsets use 32-bit ints, whole-tensor offsets 64-bit.  A ragged last
+  // tile addresses up to kRowSlack rows past N (reads there are dropped by
+  // the buffer range check), so those rows must fit too.
+  constexpr int64_t kRowSlack = 256;
   const int64_t rows = (int64_t)B * H * N;
   const int64_t tiles = ((int64_t)N + 127) / 128 * B * H;   // workgroups of the largest grid
-  const int64_t head_bytes = (int64_t)N * d * (dtype == FA_BF16 ? 2 : 4);
+  const int64_t head_bytes = ((int64_t)N + kRowSlack) * d * (dtype == FA_BF16 ? 2 : 4);
   if ((int64_t)B * H > INT32_MAX || head_bytes > INT32_MAX || tiles > INT32_MAX ||
       rows > ((int64_t)1 << 40))
     return FA_ERR_SHAPE;

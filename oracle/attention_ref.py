@@ -204,19 +204,21 @@ def forward(q, k, v, causal: bool = False, scale: Optional[float] = None):
     return _loop_heads(forward_head, (q, k, v), causal, scale)
 
 
-def forward_rows(q, k, v, rows, causal: bool = False, scale: Optional[float] = None):
+def forward_rows(q, k, v, rows, causal: bool = False, scale: Optional[float] = None,
+                 q_selected: bool = False):
     """Standard attention restricted to the query rows ``rows`` of one head.
 
     The same definition as :func:`forward_head`, evaluated only for the listed
     query indices (each output row depends on its own query row and on all of
     K and V, with the causal mask taken at the row's own index).  Used to
-    check sampled outputs of full-size problems.
+    check sampled outputs of full-size problems.  With ``q_selected`` q holds
+    just the listed rows, in the order of ``rows``.
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     rows = np.asarray(rows, dtype=np.int64)
     if scale is None:
         scale = default_scale(q.shape[-1])
-    s = scale * (q[rows] @ k.T)
+    s = scale * ((q if q_selected else q[rows]) @ k.T)
     if causal:
         cols = np.arange(k.shape[0])[None, :]
         s = np.where(cols > rows[:, None], -np.inf, s)

@@ -187,6 +187,17 @@ def test_per_head_byte_size_limit():
     assert fwd(N=1 << 22, d=128, dtype=_lib.FA_BF16, q=0) == 1
 
 
+@pytest.mark.parametrize("d,dtype,elt", [(128, _lib.FA_BF16, 2), (64, _lib.FA_BF16, 2), (128, _lib.FA_F32, 4),
+                                         (64, _lib.FA_F32, 4)])
+def test_per_head_limit_boundary_includes_the_ragged_tile_slack(d, dtype, elt):
+    # largest accepted N: (N + 256) rows of d elements within 2^31 - 1 bytes (a ragged last
+    # tile addresses up to 256 rows past N with 32-bit offsets)
+    n_max = (2**31 - 1) // (d * elt) - 256
+    assert fwd(N=n_max, d=d, dtype=dtype, q=0) == 1         # accepted: fails at the NULL check next
+    assert fwd(N=n_max + 1, d=d, dtype=dtype, q=0) == 2     # rejected as a shape error first
+    assert bwd(N=n_max + 1, d=d, dtype=dtype) == 2
+
+
 def dec(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, H=4, Nq=1, Nk=4096, d=128, causal=1, scale=0.125,
              dtype=_lib.FA_BF16, splits=0, ws=0x100000, ws_bytes=1 << 30, stream=None)

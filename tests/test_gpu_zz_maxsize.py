@@ -1,0 +1,103 @@
+"""The longest sequence the boundary accepts (needs an MI355X; about two minutes).
+
+The kernels address one head with 32-bit byte offsets, and fa_forward /
+fa_backward accept a head while (N + 256) * d * element size <= 2^31 - 1
+(a ragged last tile addresses up to 256 rows past N).  At bf16, d = 128 that
+is N = 8388351: every per-head offset is then as large as it can be, and the
+last tile is ragged.  One head, causal, inputs drawn on the device from a
+seed (workloads.device_inputs).
+
+* Forward, N(0,1) inputs: sampled query rows at both ends and in the middle,
+  each against all of its keys, compared with the oracle's definition
+  (forward_rows) at the bf16 and lse bars.
+* Backward with K = 0: every allowed key then gets the weight 1/(i+1), and the
+  definition reduces to prefix and suffix sums, written out here in fp64:
+    lse_i = ln(i+1),   O_i = (1/(i+1)) sum_{j<=i} v_j,
+    dV_j = sum_{i>=j} dO_i / (i+1),
+    dK_j = scale * sum_{i>=j} (dO_i . v_j - D_i) q_i / (i+1),  D_i = dO_i . O_i,
+    dQ = scale * dS K = 0.
+  dQ is checked whole; O, lse, dK, dV on sampled rows.
+
+Named to run last: the two tests take about two minutes together.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_tiled_attention_amd as fa
+from oracle import attention_ref as ref
+from workloads import device_inputs
+
+from gpu_helpers import TOL, TOL_LSE, announce, assert_close, require_gpu, to64
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+D = 128
+N_MAX = (2**31 - 1) // (D * 2) - 256      # bf16: the largest N the boundary accepts
+SCALE = 1.0 / math.sqrt(D)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def test_boundary_accepts_n_max_and_rejects_one_more():
+    z = torch.zeros(1, dtype=torch.bfloat16, device="cuda")
+    st = fa.fa_forward(z.data_ptr(), z.data_ptr(), z.data_ptr(), z.data_ptr(), z.data_ptr(), 1, 1, N_MAX + 1, D, 1,
+                       SCALE, 1, None)
+    assert st == 2   # FA_ERR_SHAPE, before any pointer is used
+
+
+def test_forward_at_n_max_sampled_rows():
+    announce(f"max-size forward: B=1 H=1 N={N_MAX} d={D} bf16 causal")
+    dev = torch.device("cuda", 0)
+    inp = device_inputs(1, 1, N_MAX, D, "bf16", seed=8388, device=dev)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    o, lse = fa.forward(q, k, v, causal=True, scale=SCALE)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 4097, N_MAX // 2 + 3, N_MAX - 129, N_MAX - 2, N_MAX - 1])
+    ridx = torch.as_tensor(rows, device=dev)
+    q_rows = to64(q[0, 0].index_select(0, ridx))
+    o_rows, lse_rows = o[0, 0].index_select(0, ridx).cpu(), lse[0, 0].index_select(0, ridx).cpu()
+    del o, lse, q
+    announce("max-size forward: oracle rows")
+    k64, v64 = to64(k[0, 0]), to64(v[0, 0])
+    del k, v, inp
+    torch.cuda.empty_cache()
+    o_ref, lse_ref = ref.forward_rows(q_rows, k64, v64, rows, causal=True, scale=SCALE, q_selected=True)
+    assert_close("O rows", o_rows, o_ref, TOL["bf16"], bf16_output=True)
+    assert_close("lse rows", lse_rows, lse_ref, TOL_LSE)
+
+
+def test_backward_at_n_max_zero_keys_closed_form():
+    announce(f"max-size backward (K = 0): B=1 H=1 N={N_MAX} d={D} bf16 causal")
+    dev = torch.device("cuda", 0)
+    inp = device_inputs(1, 1, N_MAX, D, "bf16", seed=8389, device=dev, names=("q", "v", "do"))
+    q, v, do = inp["q"], inp["v"], inp["do"]
+    k = torch.zeros_like(q)
+    o, lse = fa.forward(q, k, v, causal=True, scale=SCALE)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal=True, scale=SCALE)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(dq)) == 0, "dQ = scale * dS K must vanish for K = 0"
+    rows = np.array([0, 1, 777, N_MAX // 3, N_MAX - 200, N_MAX - 1])
+    ridx = torch.as_tensor(rows, device=dev)
+    got = {n: t[0, 0].index_select(0, ridx).cpu() for n, t in (("o", o), ("lse", lse), ("dk", dk), ("dv", dv))}
+    del o, lse, dq, dk, dv, k
+    announce("max-size backward: closed forms")
+    q64, v64, do64 = to64(q[0, 0]), to64(v[0, 0]), to64(do[0, 0])
+    del q, v, do, inp
+    torch.cuda.empty_cache()
+    w = 1.0 / np.arange(1, N_MAX + 1, dtype=np.float64)          # P_ij = 1/(i+1) for j <= i
+    o_all = np.cumsum(v64, axis=0)
+    o_all *= w[:, None]                                         # O_i: mean of v_0 .. v_i
+    dsum = np.einsum("nd,nd->n", do64, o_all)                   # D_i = dO_i . O_i
+    assert_close("lse rows", got["lse"], np.log(rows + 1.0), TOL_LSE)
+    assert_close("O rows", got["o"], o_all[rows], TOL["bf16"], bf16_output=True)
+    del o_all
+    dv_ref = np.stack([do64[j:].T @ w[j:] for j in rows])
+    dk_ref = np.stack([SCALE * (q64[j:].T @ ((do64[j:] @ v64[j] - dsum[j:]) * w[j:])) for j in rows])
+    assert_close("dV rows", got["dv"], dv_ref, TOL["bf16"], bf16_output=True)
+    assert_close("dK rows", got["dk"], dk_ref, TOL["bf16"], bf16_output=True)

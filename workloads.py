@@ -154,3 +154,23 @@ def fp8_inputs(B: int, H: int, N: int, d: int, seed: int, mult: float = 1.0):
         x = torch.randn((B, H, N, d), generator=g, dtype=torch.float32) * mult
         out[name] = x.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
     return out
+
+
+def device_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int, device, names=("q", "k", "v")):
+    """Seeded N(0,1) inputs drawn directly on `device` (for sequences too long
+    to draw and copy from the host in reasonable time): one device generator,
+    the tensors in the order of `names`, each drawn in fp32 in slices of at
+    most 2^26 elements and rounded once to the dtype.  A dict of device tensors."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    out = {}
+    for name in names:
+        t = torch.empty((B, H, N, d), dtype=td, device=device)
+        flat = t.view(-1)
+        step = 1 << 26
+        for i in range(0, flat.numel(), step):
+            n = min(step, flat.numel() - i)
+            flat[i:i + n] = torch.randn(n, generator=g, dtype=torch.float32, device=device).to(td)
+        out[name] = t
+    return out
