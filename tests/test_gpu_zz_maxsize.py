@@ -7,8 +7,8 @@ is N = 8388351: every per-head offset is then as large as it can be, and the
 last tile is ragged.  One head, causal, inputs drawn on the device from a
 seed (workloads.device_inputs).
 
-* Forward, N(0,1) inputs: sampled query rows at both ends and in the middle,
-  each against all of its keys, compared with the oracle's definition
+* Forward, N(0,1) inputs, scale 1: sampled query rows at both ends and in the
+  middle, each against all of its keys, compared with the oracle's definition
   (forward_rows) at the bf16 and lse bars.
 * Backward with K = 0: every allowed key then gets the weight 1/(i+1), and the
   definition reduces to prefix and suffix sums, written out here in fp64:
@@ -17,8 +17,10 @@ seed (workloads.device_inputs).
     dK_j = scale * sum_{i>=j} (dO_i . v_j - D_i) q_i / (i+1),  D_i = dO_i . O_i,
     dQ = scale * dS K = 0.
   dQ is checked whole; O, lse, dK, dV on sampled rows.
+* Split-KV decoding of 32 new queries against a cache of that length, with the
+  library's chunking and with one chunk, against the oracle's decode_head.
 
-Named to run last: the two tests take about two minutes together.
+Named to run last: together these take about two minutes.
 """
 import math
 
@@ -37,6 +39,11 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 D = 128
 N_MAX = (2**31 - 1) // (D * 2) - 256      # bf16: the largest N the boundary accepts
 SCALE = 1.0 / math.sqrt(D)
+# Forward and decoding use scale 1: scores ~ N(0, d), so each row's softmax is
+# dominated by its few largest scores and O is of order one.  At 1/sqrt(d) a
+# softmax over millions of keys is nearly uniform and O ~ mean(V) ~ 1e-3, which
+# the absolute bar could not tell from zero.
+SHARP = 1.0
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -56,7 +63,7 @@ def test_forward_at_n_max_sampled_rows():
     dev = torch.device("cuda", 0)
     inp = device_inputs(1, 1, N_MAX, D, "bf16", seed=8388, device=dev)
     q, k, v = inp["q"], inp["k"], inp["v"]
-    o, lse = fa.forward(q, k, v, causal=True, scale=SCALE)
+    o, lse = fa.forward(q, k, v, causal=True, scale=SHARP)
     torch.cuda.synchronize()
     rows = np.array([0, 1, 4097, N_MAX // 2 + 3, N_MAX - 129, N_MAX - 2, N_MAX - 1])
     ridx = torch.as_tensor(rows, device=dev)
@@ -67,7 +74,7 @@ def test_forward_at_n_max_sampled_rows():
     k64, v64 = to64(k[0, 0]), to64(v[0, 0])
     del k, v, inp
     torch.cuda.empty_cache()
-    o_ref, lse_ref = ref.forward_rows(q_rows, k64, v64, rows, causal=True, scale=SCALE, q_selected=True)
+    o_ref, lse_ref = ref.forward_rows(q_rows, k64, v64, rows, causal=True, scale=SHARP, q_selected=True)
     assert_close("O rows", o_rows, o_ref, TOL["bf16"], bf16_output=True)
     assert_close("lse rows", lse_rows, lse_ref, TOL_LSE)
 
@@ -101,3 +108,22 @@ def test_backward_at_n_max_zero_keys_closed_form():
     dk_ref = np.stack([SCALE * (q64[j:].T @ ((do64[j:] @ v64[j] - dsum[j:]) * w[j:])) for j in rows])
     assert_close("dV rows", got["dv"], dv_ref, TOL["bf16"], bf16_output=True)
     assert_close("dK rows", got["dk"], dk_ref, TOL["bf16"], bf16_output=True)
+
+
+@pytest.mark.parametrize("splits", [0, 1])
+def test_decode_at_n_max(splits):
+    # the longest cache the boundary accepts, 32 new queries (the most per call), causal;
+    # splits 0: the library's chunking (hundreds of chunks), 1: one chunk per head
+    announce(f"max-size decode: B=1 H=1 Nq=32 Nk={N_MAX} d={D} bf16 causal splits={splits}")
+    dev = torch.device("cuda", 0)
+    cache = device_inputs(1, 1, N_MAX, D, "bf16", seed=8390, device=dev, names=("k", "v"))
+    qn = device_inputs(1, 1, 32, D, "bf16", seed=8391, device=dev, names=("q",))["q"]
+    o, lse = fa.decode(qn, cache["k"], cache["v"], causal=True, scale=SHARP, num_splits=splits)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    k64, v64 = to64(cache["k"][0, 0]), to64(cache["v"][0, 0])
+    del cache
+    torch.cuda.empty_cache()
+    o_ref, lse_ref = ref.decode_head(to64(qn[0, 0]), k64, v64, causal=True, scale=SHARP)
+    assert_close("O", o[0, 0], o_ref, TOL["bf16"], bf16_output=True)
+    assert_close("lse", lse[0, 0], lse_ref, TOL_LSE)
