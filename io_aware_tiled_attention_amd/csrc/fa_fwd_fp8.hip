@@ -30,6 +30,7 @@
 // leaves room for three waves per SIMD: the vector work of one wave then
 // overlaps the matrix work of another more often.
 #include <algorithm>
+#include <type_traits>
 
 #include "fa_common.h"
 #include "fa_internal.h"
@@ -91,8 +92,11 @@ __device__ __forceinline__ f32x16 mma8(i32x8 a, i32x8 b, f32x16 c) {
 }
 
 // Four probabilities -> four E4M3 bytes of one word (round to nearest even).
+// Each conversion writes one half of the word and keeps the other; the first
+// is seeded with a's own bits (both halves end up overwritten), which spares
+// the register a zero seed would need.
 __device__ __forceinline__ int pack4_e4m3(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
@@ -107,7 +111,10 @@ void fa_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned char*
   constexpr int NC = D / 64;                   // k-chunks of the S product
   constexpr int NKB = kF8BC / 32;              // 32-key blocks per tile
   constexpr int NDB = D / 32;                  // 32-wide d blocks of O^T
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
+  // Static LDS: its base is known when the kernel is compiled, so with the
+  // loop below unrolled over the two stages every LDS read is one per-lane
+  // offset register plus an immediate.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[F8Smem<D>::BYTES];
   lds_u8* smem = (lds_u8*)smem_raw;
 
   const int tid = threadIdx.x;
@@ -186,15 +193,17 @@ void fa_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned char*
   wait_vmem();
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  // One tile: K/V of tile it in stage ST, those of tile it+1 copied into the other.
+  auto step = [&](const int it, auto stage) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage)::value;
     const int kv0 = it * kF8BC;
     if (it + 1 < ntiles) {
-      tile8_to_lds<D>(rk, L::k(smem, (it + 1) & 1), (it + 1) * kF8BC, w, lane);
-      tile8_to_lds<D>(rv, L::v(smem, (it + 1) & 1), (it + 1) * kF8BC, w, lane);
+      tile8_to_lds<D>(rk, L::k(smem, 1 - ST), (it + 1) * kF8BC, w, lane);
+      tile8_to_lds<D>(rv, L::v(smem, 1 - ST), (it + 1) * kF8BC, w, lane);
     }
 
     if (it <= wave_last) {
-      compute_st(s_cur, L::k(smem, it & 1));
+      compute_st(s_cur, L::k(smem, ST));
       const bool masked = (CAUSAL && kv0 + kF8BC - 1 > qw0) || (kv0 + kF8BC > N);
       if (masked) {
         const int last = CAUSAL ? min(N - 1, myq) : N - 1;   // keys allowed: key <= last
@@ -249,7 +258,7 @@ void fa_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned char*
         pb[2 * a + 1] = (int)sw[1];
       }
       // O^T += V^T P^T: V^T bytes 8t..8t+7 of lane (d, g) = keys 32g + 8t .. +7 of column d.
-      const lds_u8* vs = L::v(smem, it & 1);
+      const lds_u8* vs = L::v(smem, ST);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         i32x8 va;
@@ -265,7 +274,13 @@ void fa_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned char*
 
     wait_vmem();
     __syncthreads();
+  };
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    step(it + 1, std::integral_constant<int, 1>{});
   }
+  if (it < ntiles) step(it, std::integral_constant<int, 0>{});
 
   // O = v_descale * O_acc / l, lse = shift + ln l (natural log units).
   const float l_tot = pair_sum(l_run);
@@ -286,16 +301,12 @@ void fa_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned char*
 
 template <int D, bool CAUSAL>
 hipError_t launch_fp8_t(const Fp8Args& a, hipStream_t stream) {
-  constexpr int bytes = F8Smem<D>::BYTES;
-  auto kern = fa_fwd_fp8_kernel<D, CAUSAL>;
-  static const hipError_t attr_err =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (attr_err != hipSuccess) return attr_err;
+  auto kern = fa_fwd_fp8_kernel<D, CAUSAL>;   // LDS: static, F8Smem<D>::BYTES
   const int BH = a.B * a.H;
   const int n_qtiles = (a.N + kF8BR - 1) / kF8BR;
   // the scores' factor in the base-2 domain: scale * q_descale * k_descale * log2(e)
   const float kfac = std::max(a.scale * a.q_descale * a.k_descale * kLog2e, kMinFactor);
-  hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(kF8Threads), bytes, stream,
+  hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(kF8Threads), 0, stream,
                      static_cast<const unsigned char*>(a.q), static_cast<const unsigned char*>(a.k),
                      static_cast<const unsigned char*>(a.v), static_cast<bf16*>(a.o), a.lse, a.N, BH, n_qtiles,
                      wg_group(n_qtiles, 32 * 3), kfac, a.v_descale);   // 3 workgroups per CU
