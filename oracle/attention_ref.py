@@ -112,6 +112,8 @@ __all__ = [
     "expand_block_mask",
     "forward_block_sparse_head",
     "forward_block_sparse",
+    "backward_block_sparse_head",
+    "backward_block_sparse",
     "decode_head",
     "decode",
     "merge_partials",
@@ -497,6 +499,53 @@ def forward_block_sparse(q, k, v, block_mask, block_q: int, block_k: int, causal
             o[b, h], lse[b, h] = forward_block_sparse_head(q[b, h], k[b, h], v[b, h], bm[h if bm.shape[0] > 1 else 0],
                                                            block_q, block_k, causal, scale)
     return o, lse
+
+
+def backward_block_sparse_head(q, k, v, do, block_mask, block_q: int, block_k: int, causal: bool = False,
+                               scale: Optional[float] = None):
+    """Chain-rule backward of block-sparse attention for one head: (dQ, dK, dV).
+
+    The same steps as :func:`backward_head` ("Overview of Flash Attention
+    series", Backward Pass), on the P of :func:`forward_block_sparse_head`:
+    excluded entries have P = 0, so they pass no gradient, and a row that
+    keeps no entry has P = 0 throughout (its O is 0 and nothing depends on
+    its scores).
+    """
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    s = scores(q, k, scale, causal)
+    keep = expand_block_mask(block_mask, q.shape[0], k.shape[0], block_q, block_k)
+    s = np.where(keep, s, -np.inf)
+    empty = np.all(np.isneginf(s), axis=-1)
+    p = np.zeros_like(s)
+    if np.any(~empty):
+        p[~empty], _, _ = softmax_stats(s[~empty])
+    dv = p.T @ do
+    dp = do @ v.T
+    dsum = np.sum(p * dp, axis=-1)
+    ds = p * (dp - dsum[:, None])
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def backward_block_sparse(q, k, v, do, block_mask, block_q: int, block_k: int, causal: bool = False,
+                          scale: Optional[float] = None):
+    """Block-sparse backward over [B, H, N, d] inputs, one head at a time (mask as
+    in :func:`forward_block_sparse`)."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    bm = np.asarray(block_mask)
+    out = [np.empty(q.shape) for _ in range(3)]
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            g = backward_block_sparse_head(q[b, h], k[b, h], v[b, h], do[b, h], bm[h if bm.shape[0] > 1 else 0],
+                                           block_q, block_k, causal, scale)
+            for x, y in zip(out, g):
+                x[b, h] = y
+    return tuple(out)
 
 
 def decode_head(q, k, v, causal: bool = False, scale: Optional[float] = None):

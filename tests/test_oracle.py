@@ -436,6 +436,69 @@ def test_block_sparse_empty_row_is_zero_with_minus_inf_lse():
     np.testing.assert_allclose(lse_c[8:12], lse_r, rtol=1e-13)
 
 
+def _fd_block_sparse(q, k, v, g, bm, bq, bk, causal, scale, h=1e-6):
+    """Central differences of phi = sum(O * G) of the block-sparse forward oracle."""
+    out = []
+    for x in (q, k, v):
+        grad = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            keep = x[idx]
+            x[idx] = keep + h
+            op, _ = ref.forward_block_sparse_head(q, k, v, bm, bq, bk, causal, scale)
+            x[idx] = keep - h
+            om, _ = ref.forward_block_sparse_head(q, k, v, bm, bq, bk, causal, scale)
+            x[idx] = keep
+            grad[idx] = np.sum((op - om) * g) / (2 * h)
+        out.append(grad)
+    return out
+
+
+@pytest.mark.parametrize("n,bq,bk,causal", [(8, 2, 4, False), (9, 2, 2, True), (10, 4, 3, True), (7, 2, 3, False)])
+def test_block_sparse_backward_matches_finite_differences(n, bq, bk, causal):
+    """The chain rule on the block-sparse P against central differences of the
+    block-sparse forward, with masks that leave some rows empty."""
+    d = 3
+    q, k, v, g = (_rand((n, d), 750 + i + n) for i in range(4))
+    bm = _block_mask(-(-n // bq), -(-n // bk), 0.55, 60 + n + bq)
+    bm[-1, :] = 0                          # the last row block keeps nothing: O = 0, no gradient through it
+    bm[0, 0] = 1
+    dq, dk, dv = ref.backward_block_sparse_head(q, k, v, g, bm, bq, bk, causal, 0.6)
+    fq, fk, fv = _fd_block_sparse(q, k, v, g, bm, bq, bk, causal, 0.6)
+    for a, b in ((dq, fq), (dk, fk), (dv, fv)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-7)
+    assert np.all(dq[(-(-n // bq) - 1) * bq:] == 0.0)   # rows that keep no key get no dQ
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_backward_matches_torch_autograd_with_boolean_mask(causal):
+    """Independent implementation: torch SDPA in float64 with the expanded
+    boolean mask, differentiated by autograd (every row keeps a key)."""
+    n, d, bq, bk = 48, 16, 16, 8
+    q, k, v, g = (_rand((2, 3, n, d), 760 + i) for i in range(4))
+    bm = np.stack([_block_mask(3, 6, 0.45, 95 + h) for h in range(3)])
+    bm[:, :, 0] = 1
+    dq, dk, dv = ref.backward_block_sparse(q, k, v, g, bm, bq, bk, causal, 0.3)
+    keep = np.stack([ref.expand_block_mask(bm[h], n, n, bq, bk) for h in range(3)])
+    if causal:
+        keep = keep & np.tril(np.ones((n, n), dtype=bool))
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(keep)[None], scale=0.3)
+    o.backward(torch.from_numpy(g))
+    for a, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(a, t.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_backward_all_ones_is_dense(causal):
+    n, d = 40, 8
+    q, k, v, g = (_rand((n, d), 770 + i) for i in range(4))
+    ones = np.ones((3, 5), dtype=np.uint8)
+    got = ref.backward_block_sparse_head(q, k, v, g, ones, 16, 8, causal, 0.4)
+    want = ref.backward_head(q, k, v, g, causal, 0.4)
+    for a, b in zip(got, want):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
 def test_block_sparse_pins_catch_planted_mistakes():
     """A transposed block mask or masked scores set to 0 instead of excluded
     (the page's literal S o 1_M) both fail the brute-force pin."""
@@ -455,6 +518,33 @@ def test_block_sparse_pins_catch_planted_mistakes():
     assert not np.allclose(o_tr, o_b, atol=1e-6)
     o_ok, _ = ref.forward_block_sparse_head(q, k, v, bm, blk, blk, False, 0.7)
     np.testing.assert_allclose(o_ok, o_b, rtol=1e-12, atol=1e-13)
+
+
+def test_block_sparse_backward_pins_catch_planted_mistakes():
+    """Backward slips fail the finite-difference pin: the softmax row term D
+    dropped, dK's scale dropped, a transposed mask, or dV taken from dS."""
+    n, d, bq, bk = 8, 3, 4, 4
+    q, k, v, g = (_rand((n, d), 780 + i) for i in range(4))
+    bm = np.array([[1, 0], [1, 1]], dtype=np.uint8)     # not symmetric; its transpose leaves no row empty
+    fq, fk, fv = _fd_block_sparse(q, k, v, g, bm, bq, bk, False, 0.6)
+
+    def planted(which):
+        s = ref.scores(q, k, 0.6, False)
+        s = np.where(ref.expand_block_mask(bm.T if which == "mask_t" else bm, n, n, bq, bk), s, -np.inf)
+        p, _, _ = ref.softmax_stats(s)
+        dp = g @ v.T
+        dsum = 0.0 if which == "no_D" else np.sum(p * dp, axis=-1)[:, None]
+        ds = p * (dp - dsum)
+        dv = ds.T @ g if which == "dv_from_ds" else p.T @ g
+        dk = (1.0 if which == "no_scale" else 0.6) * (ds.T @ q)
+        return 0.6 * (ds @ k), dk, dv
+
+    for which in ("no_D", "no_scale", "dv_from_ds", "mask_t"):
+        got = planted(which)
+        assert not all(np.allclose(a, b, atol=1e-5) for a, b in zip(got, (fq, fk, fv))), which
+    ok = ref.backward_block_sparse_head(q, k, v, g, bm, bq, bk, False, 0.6)
+    for a, b in zip(ok, (fq, fk, fv)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-7)
 
 
 # ---------------------------------------------------------------- decoding (split-KV)
