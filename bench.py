@@ -11,14 +11,15 @@ FLOP counting convention: forward 4*B*H*N^2*d, halved when causal; backward
 2.5x forward.  The value is total (forward + backward) FLOPs per step over
 the wall time of a step, in TFLOP/s.
 
-Besides the step, "extra" carries the 4K shape, the block-sparse, decoding,
+Besides the step, "extra" carries the 4K shape, the block-sparse (forward and
+backward), decoding,
 dropout and FP8 paths, and the library GEMM's rate on N(0,1) operands in the
 same run (the practical matrix-core ceiling for such data, with each kernel's
 fraction of it).
 
 Prints ONE JSON line.  Options: --gpus N (only 1: the path runs on one GPU),
 --steps K, --warmup W, --no-cpu-baseline, --no-extra, --decode-only, --dropout-only,
---fp8-only.
+--fp8-only, --sparse-only.
 """
 from __future__ import annotations
 
@@ -191,20 +192,24 @@ def kept_pairs(mask, n, bq, bk, causal):
 
 
 def sparse_measurement(fa, torch, dev, steps):
-    """Block-sparse forward on the 16K causal d=128 shape with a sliding-window
-    plus global-column mask; FLOPs counted on the kept (query, key) pairs
-    only, and the dense causal forward on the same inputs for comparison."""
+    """Block-sparse forward and backward on the 16K causal d=128 shape with a
+    sliding-window plus global-column mask; FLOPs counted on the kept
+    (query, key) pairs only (backward: 2.5x the forward's), and the dense
+    causal forward and backward on the same inputs for comparison."""
     from workloads import PROBLEMS, block_mask, make_inputs
-    p = PROBLEMS["causal_16k_d128"]
+    p = PROBLEMS["causal_16k_d128_bwd"]
     bq = bk = 128
     window = 8                       # key blocks before the diagonal (1024 keys)
     mask = block_mask(1, p.N, bq, bk, "local_global", seed=0, window=window).to(dev)
-    inputs = make_inputs(p)
-    q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
+    inputs = make_inputs(p, with_do=True)
+    q, k, v, do = (inputs[n].to(dev) for n in ("q", "k", "v", "do"))
     o = torch.empty_like(q)
     lse = torch.empty((p.B, p.H, p.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     stream = torch.cuda.current_stream().cuda_stream
     raw = fa.load_library()
+    ws_n = raw.fa_backward_workspace_size(p.B, p.H, p.N, p.d)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
 
     def run_sparse():
         st = raw.fa_forward_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -228,7 +233,24 @@ def sparse_measurement(fa, torch, dev, steps):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
+    def run_sparse_bwd():
+        st = raw.fa_backward_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                          lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                          mask.data_ptr(), 1, bq, bk, p.B, p.H, p.N, p.d, 1, p.scale, 1,
+                                          ws.data_ptr(), ws_n, stream)
+        assert st == 0, st
+
+    def run_dense_bwd():
+        st = raw.fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), p.B, p.H, p.N, p.d, 1, p.scale, 1,
+                             ws.data_ptr(), ws_n, stream)
+        assert st == 0, st
+
     ms_s, ms_d = timed(run_sparse), timed(run_dense)
+    run_sparse()                    # O and lse of the masked problem for its backward
+    ms_sb = timed(run_sparse_bwd)
+    run_dense()
+    ms_db = timed(run_dense_bwd)
     pairs = kept_pairs(mask, p.N, bq, bk, True)[0] * p.B * p.H
     dense_pairs = p.N * (p.N + 1) // 2 * p.B * p.H
     flops = 4.0 * p.d * pairs
@@ -236,7 +258,9 @@ def sparse_measurement(fa, torch, dev, steps):
                         f"{window} key blocks plus the first key block column",
             "kept_fraction_of_causal_pairs": pairs / dense_pairs, "ms": ms_s, "dense_causal_ms": ms_d,
             "tflops_on_kept_pairs": flops / ms_s * 1e-9, "frac_peak": flops / ms_s * 1e-9 / PEAK_BF16_TFLOPS,
-            "speedup_vs_dense_causal": ms_d / ms_s}
+            "speedup_vs_dense_causal": ms_d / ms_s,
+            "bwd_ms": ms_sb, "dense_causal_bwd_ms": ms_db, "bwd_tflops_on_kept_pairs": 2.5 * flops / ms_sb * 1e-9,
+            "bwd_frac_peak": 2.5 * flops / ms_sb * 1e-9 / PEAK_BF16_TFLOPS, "bwd_speedup_vs_dense_causal": ms_db / ms_sb}
 
 
 def dropout_measurement(fa, torch, dev, steps, p_drop=0.1):
@@ -486,6 +510,8 @@ def main(argv=None):
                          "split-KV decoding, dropout, FP8 forward)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the split-KV decoding measurement (one JSON line; for kernel traces)")
+    ap.add_argument("--sparse-only", action="store_true",
+                    help="only the block-sparse forward and backward measurement (one JSON line)")
     ap.add_argument("--fp8-only", action="store_true",
                     help="only the FP8 forward measurement (one JSON line; for kernel traces)")
     ap.add_argument("--dropout-only", action="store_true",
@@ -521,6 +547,9 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": {"bytes_read_per_copy": 4 * n, "bytes_written_per_copy": 4 * n,
                                                "copies": 3}}), flush=True)
+        return 0
+    if args.sparse_only:
+        print(json.dumps({"block_sparse_16k_d128": sparse_measurement(fa, torch, dev, max(3, args.steps))}), flush=True)
         return 0
     if args.fp8_only:
         print(json.dumps({"fp8_16k_d128": fp8_measurement(fa, torch, dev, max(3, args.steps))}), flush=True)

@@ -157,6 +157,25 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Block-sparse backward pass: the gradients of fa_forward_block_sparse
+ * ("Overview of Flash Attention series", section Block-sparse
+ * Flashattention: the backward skips the same zero blocks as the forward).
+ * Inputs O and lse come from fa_forward_block_sparse with the same mask,
+ * mask_heads, block_q, block_k, causal and scale; the mask arguments follow
+ * the same rules (FA_ERR_MASK otherwise), everything else as fa_backward
+ * (the workspace is fa_backward_workspace_size bytes).  Blocks the mask
+ * removes get no gradient, and rows that keep no key get dQ = 0.  The
+ * preprocess pass (D = rowsum(dO o O)) runs over every row; the dK/dV and
+ * dQ passes visit only kept blocks, so their work scales with the kept
+ * fraction.  Deterministic (no atomics).
+ */
+int fa_backward_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             const unsigned char* block_mask, int mask_heads, int block_q, int block_k,
+                             int B, int H, int N, int d, int causal, float scale, int dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Forward with 8-bit float inputs.  q, k, v: [B,H,N,d] in the OCP FP8 format
  * E4M3 (one byte per element: sign, 4 exponent bits with bias 7, 3 mantissa
  * bits, subnormals, no infinities, largest finite 448), each tensor with one

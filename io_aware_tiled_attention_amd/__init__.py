@@ -9,6 +9,7 @@ contiguous [B, H, N, d] in float32 or bfloat16 on a ROCm device; lse is
     o, lse = forward(q, k, v, causal=True)
     dq, dk, dv = backward(q, k, v, o, do, lse, causal=True)
     o, lse = forward_block_sparse(q, k, v, block_mask, block_q=128, block_k=64)
+    dq, dk, dv = backward_block_sparse(q, k, v, o, do, lse, block_mask, block_q=128, block_k=64)
 """
 from __future__ import annotations
 
@@ -16,13 +17,15 @@ import math
 from typing import Optional, Tuple
 
 from . import _lib
-from ._lib import (FA_BF16, FA_F32, FaError, fa_backward, fa_backward_dkdv, fa_backward_dq, fa_backward_dropout,
+from ._lib import (FA_BF16, FA_F32, FaError, fa_backward, fa_backward_block_sparse, fa_backward_dkdv,
+                   fa_backward_dq, fa_backward_dropout,
                    fa_backward_preprocess, fa_backward_workspace_size, fa_decode, fa_decode_num_splits,
                    fa_decode_workspace_size, fa_forward, fa_forward_block_sparse, fa_forward_dropout,
                    fa_forward_fp8, fa_strerror)
 
-__all__ = ["forward", "forward_block_sparse", "forward_fp8", "backward", "decode", "workspace_size", "FaError", "FA_F32",
-           "FA_BF16", "fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_size",
+__all__ = ["forward", "forward_block_sparse", "forward_fp8", "backward", "backward_block_sparse", "decode",
+           "workspace_size", "FaError", "FA_F32", "FA_BF16", "fa_forward", "fa_forward_block_sparse", "fa_backward",
+           "fa_backward_block_sparse", "fa_backward_workspace_size",
            "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_forward_dropout",
            "fa_backward_dropout", "fa_forward_fp8", "fa_decode",
            "fa_decode_workspace_size", "fa_decode_num_splits", "fa_strerror", "load_library",
@@ -166,6 +169,38 @@ def forward_block_sparse(q, k, v, block_mask, block_q: int, block_k: int, causal
     if st != 0:
         raise FaError(st, "fa_forward_block_sparse")
     return out, lse
+
+
+def backward_block_sparse(q, k, v, o, do, lse, block_mask, block_q: int, block_k: int, causal: bool = False,
+                          scale: Optional[float] = None, dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV of :func:`forward_block_sparse` for the upstream gradient dO
+    (o and lse from that forward with the same mask, blocks, causal, scale)."""
+    import torch
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(name, t, q.shape, q.dtype, q.device)
+    _check("lse", lse, (B, H, N), torch.float32, q.device)
+    if block_mask.dim() != 3:
+        raise ValueError("block_mask must be [Hm, ceil(N / block_q), ceil(N / block_k)]")
+    tq, tk = -(-N // block_q), -(-N // block_k)
+    _check("block_mask", block_mask, (block_mask.shape[0], tq, tk), torch.uint8, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, q.shape, q.dtype, q.device)
+    need = fa_backward_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = fa_backward_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), block_mask.data_ptr(),
+                                  block_mask.shape[0], block_q, block_k, B, H, N, d, causal, scale, _dtype_code(q),
+                                  workspace.data_ptr(), workspace.numel(), _stream_ptr(q.device))
+    if st != 0:
+        raise FaError(st, "fa_backward_block_sparse")
+    return dq, dk, dv
 
 
 def decode(q, k, v, causal: bool = True, scale: Optional[float] = None, num_splits: int = 0,

@@ -20,7 +20,8 @@ STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_DTYPE",
     5: "FA_ERR_SCALE", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ALIGN", 9: "FA_ERR_MASK", 10: "FA_ERR_DROPOUT",
 }
-EXPORTED = ("fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_workspace_size",
+EXPORTED = ("fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_block_sparse",
+            "fa_backward_workspace_size",
             "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_forward_dropout",
             "fa_backward_dropout", "fa_forward_fp8", "fa_decode",
             "fa_decode_workspace_size", "fa_decode_num_splits", "fa_strerror")
@@ -55,6 +56,9 @@ def load() -> ctypes.CDLL:
         lib.fa_forward_block_sparse.restype = i
         lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
         lib.fa_backward.restype = i
+        lib.fa_backward_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                                 f, i, vp, sz, vp]
+        lib.fa_backward_block_sparse.restype = i
         lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
         lib.fa_backward_workspace_size.restype = sz
         lib.fa_backward_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
@@ -97,6 +101,13 @@ def fa_backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dt
                 workspace, workspace_bytes, stream) -> int:
     return load().fa_backward(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, int(causal),
                               float(scale), dtype, workspace, workspace_bytes, stream)
+
+
+def fa_backward_block_sparse(q, k, v, o, dout, lse, dq, dk, dv, block_mask, mask_heads, block_q, block_k, B, H, N,
+                             d, causal, scale, dtype, workspace, workspace_bytes, stream) -> int:
+    return load().fa_backward_block_sparse(q, k, v, o, dout, lse, dq, dk, dv, block_mask, mask_heads, block_q,
+                                           block_k, B, H, N, d, int(bool(causal)), scale, dtype, workspace,
+                                           workspace_bytes, stream)
 
 
 def fa_backward_preprocess(o, dout, lse, B, H, N, d, dtype, workspace, workspace_bytes, stream) -> int:

@@ -39,10 +39,25 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 // Validation and launch for any subset of the backward stages.  A pointer is
 // required (non-NULL, 16-byte aligned) exactly when a requested stage reads
 // or writes it.
+// Block-mask geometry shared by the block-sparse forward and backward.
+int check_mask(int H, int N, int mask_heads, int block_q, int block_k) {
+  if (block_q <= 0 || block_q % 32 != 0 || block_k <= 0 || block_k % 64 != 0 || N > fa::kSparseMaxN ||
+      (mask_heads != 1 && mask_heads != H))
+    return FA_ERR_MASK;
+  return FA_OK;
+}
+
+// A block mask for the backward: `mask` non-NULL selects the block-sparse
+// kernels (geometry already checked with check_mask).
+struct BwdMask {
+  const unsigned char* mask = nullptr;
+  int mask_heads = 0, block_q = 0, block_k = 0;
+};
+
 int run_backward(int stages, const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal,
                  float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream,
-                 const fa::DropParams& drop = fa::DropParams{}) {
+                 const fa::DropParams& drop = fa::DropParams{}, const BwdMask& bm = BwdMask{}) {
   bool empty = false;
   const int st = check_shape(B, H, N, d, dtype, scale, &empty);
   if (st != FA_OK) return st;
@@ -74,6 +89,10 @@ int run_backward(int stages, const void* q, const void* k, const void* v, const 
   char* ws = static_cast<char*>(workspace);
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal ? 1 : 0, dtype, scale,
                 reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + fa::ws_dsum_bytes(rows)), drop};
+  a.mask = bm.mask;
+  a.mask_heads = bm.mask_heads;
+  a.block_q = bm.block_q;
+  a.block_k = bm.block_k;
   return hip_status(fa::launch_backward(a, stages, static_cast<hipStream_t>(stream)));
 }
 
@@ -147,14 +166,29 @@ int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o
   bool empty = false;
   const int st = check_shape(B, H, N, d, dtype, scale, &empty);
   if (st != FA_OK) return st;
-  if (block_q <= 0 || block_q % 32 != 0 || block_k <= 0 || block_k % 64 != 0 || N > fa::kSparseMaxN ||
-      (mask_heads != 1 && mask_heads != H))
-    return FA_ERR_MASK;
+  const int ms = check_mask(H, N, mask_heads, block_q, block_k);
+  if (ms != FA_OK) return ms;
   if (empty) return FA_OK;
   if (!q || !k || !v || !o || !lse || !block_mask) return FA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
   fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal ? 1 : 0, dtype, scale, block_mask, mask_heads, block_q, block_k};
   return hip_status(fa::launch_forward(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_backward_block_sparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, void* dq, void* dk, void* dv, const unsigned char* block_mask,
+                             int mask_heads, int block_q, int block_k, int B, int H, int N, int d, int causal,
+                             float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  const int st = check_shape(B, H, N, d, dtype, scale, &empty);
+  if (st != FA_OK) return st;
+  const int ms = check_mask(H, N, mask_heads, block_q, block_k);
+  if (ms != FA_OK) return ms;
+  if (empty) return FA_OK;
+  if (!block_mask) return FA_ERR_NULL;
+  return run_backward(fa::kStagePre | fa::kStageDkDv | fa::kStageDq, q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d,
+                      causal, scale, dtype, workspace, workspace_bytes, stream, fa::DropParams{},
+                      BwdMask{block_mask, mask_heads, block_q, block_k});
 }
 
 // Decode shapes: Nq in [0, 32], Nk >= 1 unless the problem is empty, causal needs Nq <= Nk.

@@ -44,6 +44,7 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = kBwdWaves * 64;
 constexpr int kBwdKW = 32;                      // keys per wave
 constexpr int kBwdBK = kBwdWaves * kBwdKW;      // keys per workgroup
+constexpr int kBwdListCap = 2 * kListMax;         // block-sparse list of 32-row query blocks (fp32)
 
 template <typename T, int D>
 struct BwdCfg {
@@ -92,12 +93,12 @@ void fa_bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, const 
 }
 
 // ---------------------------------------------------------------- 2. dK, dV
-template <typename T, int D, bool CAUSAL, bool DROP>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(kBwdThreads, 2)
 void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                         const T* __restrict__ dO, const float* __restrict__ dsum, const float* __restrict__ nlse,
                         T* __restrict__ dK, T* __restrict__ dV, int N, int BH, int n_ktiles, int group, float scale,
-                        DropParams dpar) {
+                        SparseArgs sp, DropParams dpar) {
   using M = Mfma<T>;
   using C = BwdCfg<T, D>;
   using G = Tile<T, D>;                 // Q and dO tiles: BQ rows x D
@@ -237,15 +238,52 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
   const int q_begin = CAUSAL ? k0 : 0;
   const int nblocks = (N - q_begin + BQ - 1) / BQ;
 
-  load_block(q_begin, 0);
+  // The query blocks visited: all from q_begin (dense), or those the block
+  // mask keeps for some (sub-block, wave) pair, bit qs_i * waves + wave
+  // (block-sparse; each 32-row sub-block lies in one mask row, each wave's
+  // 32 keys in one mask column).
+  const TileList tl = tile_list_at<kBwdListCap>(smem + C::BYTES);
+  int n_act = nblocks;
+  if constexpr (SPARSE) {
+    const int tk_n = (N + sp.block_k - 1) / sp.block_k;
+    const int tq_n = (N + sp.block_q - 1) / sp.block_q;
+    const unsigned char* mrow = mask_of_head(sp.mask, bh, sp.H, sp.mask_heads, tq_n, tk_n);
+    n_act = build_tile_list<kBwdWaves>(
+        nblocks,
+        [&](int b) -> unsigned {
+          unsigned bits = 0;
+#pragma unroll
+          for (int qs_i = 0; qs_i < QB; ++qs_i)
+#pragma unroll
+            for (int w2 = 0; w2 < kBwdWaves; ++w2) {
+              const int kw = k0 + w2 * kBwdKW;
+              const int qs = q_begin + b * BQ + qs_i * 32;
+              const bool reach = kw < N && qs < N && !(CAUSAL && qs + 31 < kw);
+              if (reach && mrow[(qs / sp.block_q) * tk_n + kw / sp.block_k] != 0)
+                bits |= 1u << (qs_i * kBwdWaves + w2);
+            }
+          return bits;
+        },
+        tl, tid, w, lane);
+  } else {
+    (void)sp;
+  }
+  auto block_of = [&](int i) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)tl.act[i]);
+    else return i;
+  };
+
+  if (n_act > 0) load_block(q_begin + block_of(0) * BQ, 0);
   wait_vmem();
   __syncthreads();
 
-  for (int it = 0; it < nblocks; ++it) {
-    const int q0b = q_begin + it * BQ;
+  for (int it = 0; it < n_act; ++it) {
+    const int q0b = q_begin + block_of(it) * BQ;
     q_blk = q0b;
     const int st = it & 1;
-    if (it + 1 < nblocks) load_block(q0b + BQ, st ^ 1);
+    if (it + 1 < n_act) load_block(q_begin + block_of(it + 1) * BQ, st ^ 1);
+    unsigned wbits = 0xFFu;
+    if constexpr (SPARSE) wbits = (unsigned)__builtin_amdgcn_readfirstlane((int)tl.wbit[it]);
 
     const lds_u8* qs = C::q(smem, st);
     const lds_u8* dos = C::dout(smem, st);
@@ -259,6 +297,7 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
       const int qsb = q0b + qs_i * 32;
       // every query of the sub-block precedes every key of the wave: nothing to add
       if (CAUSAL && !full && qsb + 31 < kw0) continue;
+      if (SPARSE && !((wbits >> (qs_i * kBwdWaves + w)) & 1)) continue;   // block masked out
       __builtin_amdgcn_iglp_opt(2);   // interleave the exponentials with the products
       f32x16 s, dp;
       sdp(qs, dos, qs_i, s, dp);
@@ -322,12 +361,12 @@ struct KvCfg {
   static_assert(STAGE + DO0 + 16 * G::R < 65536, "stage offsets fit the ds_read immediate");
 };
 
-template <int D, bool CAUSAL, bool DROP>
+template <int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(kKvThreads, 1)
 void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                              const bf16* __restrict__ dO, const float* __restrict__ dsum,
                              const float* __restrict__ nlse, bf16* __restrict__ dK, bf16* __restrict__ dV, int N,
-                             int BH, int n_ktiles, int group, float scale, DropParams dpar) {
+                             int BH, int n_ktiles, int group, float scale, SparseArgs sp, DropParams dpar) {
   using M = Mfma<bf16>;
   using C = KvCfg<D>;
   using G = Tile<bf16, D>;
@@ -337,8 +376,9 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   constexpr int KPL = M::KPL, KC = M::KC;
   constexpr int NDB = D / 32, NC = D / KC, BQ = C::BQ;
-  // static, so that every LDS address is known at compile time
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[C::BYTES];
+  // static, so that every LDS address is known at compile time (block-sparse:
+  // the query-block list follows)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[C::BYTES + (SPARSE ? kListBytes : 0)];
   lds_u8* smem = (lds_u8*)smem_raw;
 
   const int tid = threadIdx.x;
@@ -410,28 +450,62 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
   const int q_begin = CAUSAL ? k0 : 0;
   const int nblocks = (N - q_begin + BQ - 1) / BQ;
 
+  // The query blocks this workgroup visits: all from q_begin (dense), or the
+  // ones the block mask keeps for some wave (block-sparse; a wave's 32 keys
+  // lie in one mask column since block_k is a multiple of 64, its 32-row
+  // half of a block in one mask row since block_q is a multiple of 32).
+  const TileList tl = tile_list_at(smem + C::BYTES);
+  int n_act = nblocks;
+  if constexpr (SPARSE) {
+    const int tk_n = (N + sp.block_k - 1) / sp.block_k;
+    const int tq_n = (N + sp.block_q - 1) / sp.block_q;
+    const unsigned char* mrow = mask_of_head(sp.mask, bh, sp.H, sp.mask_heads, tq_n, tk_n);
+    n_act = build_tile_list<kKvWaves>(
+        nblocks,
+        [&](int b) -> unsigned {
+          unsigned bits = 0;
+#pragma unroll
+          for (int w2 = 0; w2 < kKvWaves; ++w2) {
+            const int kw = k0 + (w2 & 3) * kBwdKW;
+            const int qs = q_begin + b * BQ + (w2 >> 2) * 32;
+            const bool reach = kw < N && qs < N && !(CAUSAL && qs + 31 < kw);
+            if (reach && mrow[(qs / sp.block_q) * tk_n + kw / sp.block_k] != 0) bits |= 1u << w2;
+          }
+          return bits;
+        },
+        tl, tid, w, lane);
+  } else {
+    (void)sp;
+  }
+  auto block_of = [&](int i) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)tl.act[i]);
+    else return i;
+  };
+
   tile_to_lds_async<bf16, D, kBwdBK, kKvWaves>(rk, smem + C::KOFF, k0, w, lane);
   tile_to_lds_async<bf16, D, kBwdBK, kKvWaves>(rv, smem + C::VOFF, k0, w, lane);
-  load_block(q_begin, 0);
+  if (n_act > 0) load_block(q_begin + block_of(0) * BQ, 0);
   wait_vmem();
   __syncthreads();
   Frag kf[NC];   // this wave's K slice as B fragments, read once
 #pragma unroll
   for (int c = 0; c < NC; ++c) kf[c] = M::lds(smem + ka[c]);
 
-  // One 64-row query block from staging buffer ST; MASKED also handles the
-  // causal diagonal and keys past the end of the sequence.
+  // Visited query block number `it` (64 rows from q_begin + block_of(it) * 64)
+  // from staging buffer ST; MASKED also handles the causal diagonal and keys
+  // past the end of the sequence.
   auto block = [&](int it, auto st_c, auto masked_c) {
     constexpr int ST = decltype(st_c)::value;
     constexpr bool MASKED = decltype(masked_c)::value;
-    const int q0b = q_begin + it * BQ;
-    if (it + 1 < nblocks) load_block(q0b + BQ, ST ^ 1);
+    const int q0b = q_begin + block_of(it) * BQ;
+    if (it + 1 < n_act) load_block(q_begin + block_of(it + 1) * BQ, ST ^ 1);
     const int qsb = q0b + grp * 32;   // this wave's 32 query rows
     bool run = true, diag = false;
     if constexpr (MASKED) {
       run = !(CAUSAL && qsb + 31 < kw0);   // some query reaches some key of the slice
       diag = (CAUSAL && qsb < kw0 + kBwdKW - 1) || (kw0 + kBwdKW > N);
     }
+    if constexpr (SPARSE) run = run && ((__builtin_amdgcn_readfirstlane((int)tl.wbit[it]) >> w) & 1);
     if (run) {
       const lds_u8* sb = smem + ST * C::STAGE;
       // DROP: this block's random bytes, generated before the products so
@@ -518,9 +592,14 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
   using Msk = std::integral_constant<bool, true>;
   using NoMsk = std::integral_constant<bool, false>;
   // Blocks 0 and 1 hold the causal diagonal of the 128 keys; a key tile that
-  // reaches past the end of the sequence is masked throughout.
+  // reaches past the end of the sequence is masked throughout.  Block-sparse:
+  // the visited blocks among those two (the list is in increasing order),
+  // rounded up to an even count -- the masked body is correct for any block.
   const bool ktail = k0 + kBwdBK > N;
-  const int n_masked = ktail ? nblocks : (CAUSAL ? min(2, nblocks) : 0);
+  int n_masked = ktail ? n_act : (CAUSAL ? min(2, n_act) : 0);
+  if constexpr (SPARSE) {
+    if (!ktail && CAUSAL) n_masked = (n_act > 0 && block_of(0) < 2) ? min(2, n_act) : 0;
+  }
   int it = 0;
   for (; it < n_masked; it += 2) {
     block(it, S0{}, Msk{});
@@ -529,9 +608,9 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
   }
   // n_masked is even unless it covers every block, so the unmasked blocks
   // start on staging buffer 0.
-  for (; it < nblocks; it += 2) {
+  for (; it < n_act; it += 2) {
     block(it, S0{}, NoMsk{});
-    if (it + 1 >= nblocks) break;
+    if (it + 1 >= n_act) break;
     block(it + 1, S1{}, NoMsk{});
   }
 
@@ -582,11 +661,12 @@ constexpr int kDqBR = kDqWaves * kDqQW;         // query rows per workgroup
 constexpr int kDqBC = 64;                       // keys per K/V tile
 constexpr int kDqThreads = kDqWaves * 64;
 
-template <typename T, int D, bool CAUSAL, bool DROP>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(kDqThreads, sizeof(T) == 2 ? 2 : 1)
 void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                       const T* __restrict__ dO, const float* __restrict__ dsum, const float* __restrict__ nlse,
-                      T* __restrict__ dQ, int N, int BH, int n_qtiles, int group, float scale, DropParams dpar) {
+                      T* __restrict__ dQ, int N, int BH, int n_qtiles, int group, float scale, SparseArgs sp,
+                      DropParams dpar) {
   using M = Mfma<T>;
   using G = Tile<T, D>;
   using X = ExpDomain<T>;
@@ -638,6 +718,40 @@ void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
   const int ntiles = (kv_end + kDqBC - 1) / kDqBC;
   const int wave_last = CAUSAL ? min(ntiles - 1, (qw0 + kDqQW - 1) / kDqBC) : ntiles - 1;
 
+  // The key tiles visited: all up to kv_end (dense) or those the block mask
+  // keeps for some wave (block-sparse, as in the bf16 kernel).
+  const TileList tl = tile_list_at(smem + 4 * TILE);
+  int n_act = ntiles;
+  if constexpr (SPARSE) {
+    const int tk_n = (N + sp.block_k - 1) / sp.block_k;
+    const int tq_n = (N + sp.block_q - 1) / sp.block_q;
+    const unsigned char* mrow = mask_of_head(sp.mask, bh, sp.H, sp.mask_heads, tq_n, tk_n);
+    n_act = build_tile_list<kDqWaves>(
+        ntiles,
+        [&](int jj) -> unsigned {
+          const int kb = jj * kDqBC / sp.block_k;
+          unsigned bits = 0;
+#pragma unroll
+          for (int w2 = 0; w2 < kDqWaves; ++w2) {
+            const int qw = q0 + w2 * kDqQW;
+            const bool reach = qw < N && !(CAUSAL && jj * kDqBC > qw + kDqQW - 1);
+            if (reach && mrow[(qw / sp.block_q) * tk_n + kb] != 0) bits |= 1u << w2;
+          }
+          return bits;
+        },
+        tl, tid, w, lane);
+  } else {
+    (void)sp;
+  }
+  auto tile_of = [&](int i) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)tl.act[i]);
+    else return i;
+  };
+  auto active = [&](int i) -> bool {
+    if constexpr (SPARSE) return (__builtin_amdgcn_readfirstlane((int)tl.wbit[i]) >> w) & 1;
+    else return i <= wave_last;
+  };
+
   auto load_tile = [&](int j, int st) {
     tile_to_lds<T, D, kDqBC, kDqWaves>(rk, smem + st * TILE, j * kDqBC, w, lane);
     tile_to_lds<T, D, kDqBC, kDqWaves>(rv, smem + (2 + st) * TILE, j * kDqBC, w, lane);
@@ -647,15 +761,16 @@ void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-  load_tile(0, 0);
+  if (n_act > 0) load_tile(tile_of(0), 0);
   wait_vmem();
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int st = j & 1;
+  for (int it = 0; it < n_act; ++it) {
+    const int st = it & 1;
+    const int j = tile_of(it);
     const int kv0 = j * kDqBC;
-    if (j + 1 < ntiles) load_tile(j + 1, st ^ 1);
-    if (j <= wave_last) {
+    if (it + 1 < n_act) load_tile(tile_of(it + 1), st ^ 1);
+    if (active(it)) {
       const lds_u8* ks = smem + st * TILE;
       const lds_u8* vs = smem + (2 + st) * TILE;
       // S^T = K Q^T and dP^T = V dO^T: rows = keys, column = this lane's query.
@@ -735,12 +850,12 @@ void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
 // The two 32-key halves of a tile are processed one after the other so that
 // the first half's dS is already packed to bf16 while the second half's
 // products run.
-template <int D, bool CAUSAL, bool DROP>
+template <int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(kDqThreads, 2)
 void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                            const bf16* __restrict__ dO, const float* __restrict__ dsum,
                            const float* __restrict__ nlse, bf16* __restrict__ dQ, int N, int BH, int n_qtiles,
-                           int group, float scale, DropParams dpar) {
+                           int group, float scale, SparseArgs sp, DropParams dpar) {
   using M = Mfma<bf16>;
   using G = Tile<bf16, D>;
   using X = ExpDomain<bf16>;
@@ -750,8 +865,8 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   constexpr int NKB = kDqBC / 32;
   constexpr int NDB = D / 32, NC = D / KC;
   constexpr int TILE = kDqBC * G::R;
-  // [K st0][K st1][V st0][V st1]
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[4 * TILE];
+  // [K st0][K st1][V st0][V st1] (block-sparse: then the tile list)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[4 * TILE + (SPARSE ? kListBytes : 0)];
   lds_u8* smem = (lds_u8*)smem_raw;
 
   const int tid = threadIdx.x;
@@ -765,6 +880,7 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   const int bh = wo.bh;
   const int qt = CAUSAL ? n_qtiles - 1 - wo.rank : wo.rank;
   const int q0 = qt * kDqBR;
+  if constexpr (!SPARSE) (void)sp;
   const size_t head = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * G::R;
   const rsrc_t rq = make_rsrc(Q + head, head_bytes);
@@ -810,6 +926,42 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   const int ntiles = (kv_end + kDqBC - 1) / kDqBC;
   const int wave_last = CAUSAL ? min(ntiles - 1, (qw0 + kDqQW - 1) / kDqBC) : ntiles - 1;
 
+  // The key tiles this workgroup visits: all up to kv_end (dense) or the
+  // ones the block mask keeps for some wave (block-sparse; each wave's 32
+  // rows lie in one mask row since block_q is a multiple of 32, and each
+  // 64-key tile in one mask column since block_k is a multiple of 64).  A
+  // wave that reaches a tile has every one of its rows past the tile's first
+  // key, so no row it computes has lse = -inf.
+  const TileList tl = tile_list_at(smem + 4 * TILE);
+  int n_act = ntiles;
+  if constexpr (SPARSE) {
+    const int tk_n = (N + sp.block_k - 1) / sp.block_k;
+    const int tq_n = (N + sp.block_q - 1) / sp.block_q;
+    const unsigned char* mrow = mask_of_head(sp.mask, bh, sp.H, sp.mask_heads, tq_n, tk_n);
+    n_act = build_tile_list<kDqWaves>(
+        ntiles,
+        [&](int j) -> unsigned {
+          const int kb = j * kDqBC / sp.block_k;
+          unsigned bits = 0;
+#pragma unroll
+          for (int w2 = 0; w2 < kDqWaves; ++w2) {
+            const int qw = q0 + w2 * kDqQW;
+            const bool reach = qw < N && !(CAUSAL && j * kDqBC > qw + kDqQW - 1);
+            if (reach && mrow[(qw / sp.block_q) * tk_n + kb] != 0) bits |= 1u << w2;
+          }
+          return bits;
+        },
+        tl, tid, w, lane);
+  }
+  auto tile_of = [&](int i) -> int {
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)tl.act[i]);
+    else return i;
+  };
+  auto active = [&](int i) -> bool {
+    if constexpr (SPARSE) return (__builtin_amdgcn_readfirstlane((int)tl.wbit[i]) >> w) & 1;
+    else return i <= wave_last;
+  };
+
   auto load_tile = [&](int j, int st) {
     tile_to_lds_async<bf16, D, kDqBC, kDqWaves>(rk, smem + st * TILE, j * kDqBC, w, lane);
     tile_to_lds_async<bf16, D, kDqBC, kDqWaves>(rv, smem + (2 + st) * TILE, j * kDqBC, w, lane);
@@ -819,17 +971,19 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-  load_tile(0, 0);
+  if (n_act > 0) load_tile(tile_of(0), 0);
   wait_vmem();
   __syncthreads();
 
-  auto tile = [&](int j, auto st_c, auto masked_c) {
+  // Visited tile number `it` (tile_of(it)) from staging buffer ST.
+  auto tile = [&](int it, auto st_c, auto masked_c) {
     constexpr int ST = decltype(st_c)::value;
     constexpr bool MASKED = decltype(masked_c)::value;
     constexpr int KB = ST * TILE, VB = (2 + ST) * TILE;
+    const int j = tile_of(it);
     const int kv0 = j * kDqBC;
-    if (j + 1 < ntiles) load_tile(j + 1, ST ^ 1);
-    if (!MASKED || j <= wave_last) {
+    if (it + 1 < n_act) load_tile(tile_of(it + 1), ST ^ 1);
+    if (!MASKED || active(it)) {
       bool msk = false;
       int last = 0;
       if constexpr (MASKED) {
@@ -918,8 +1072,11 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   using Msk = std::integral_constant<bool, true>;
   using NoMsk = std::integral_constant<bool, false>;
   // Leading tiles that no wave needs to mask: keys below the workgroup's
-  // first query (causal), or all whole tiles (non-causal).
-  const int n_plain = CAUSAL ? min(ntiles, q0 / kDqBC) : N / kDqBC;
+  // first query (causal), or all whole tiles (non-causal).  Block-sparse:
+  // every visited tile takes the masked body, which also skips the waves
+  // the mask leaves out (the causal / tail masking inside is a uniform
+  // branch taken only where needed).
+  const int n_plain = SPARSE ? 0 : (CAUSAL ? min(ntiles, q0 / kDqBC) : N / kDqBC);
   int j = 0;
   for (; j + 1 < n_plain; j += 2) {
     tile(j, S0{}, NoMsk{});
@@ -929,7 +1086,7 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
     tile(j, S0{}, NoMsk{});
     ++j;
   }
-  for (; j < ntiles; ++j) {
+  for (; j < n_act; ++j) {
     if (j & 1) tile(j, S1{}, Msk{});
     else tile(j, S0{}, Msk{});
   }
@@ -944,12 +1101,14 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
                    acc[db][4 * a + 1] * scale, acc[db][4 * a + 2] * scale, acc[db][4 * a + 3] * scale);
 }
 
-template <typename T, int D, bool CAUSAL, bool DROP>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   const int BH = a.B * a.H;
   const size_t rows = (size_t)BH * a.N;
   const int n_ktiles = (a.N + kBwdBK - 1) / kBwdBK;
   const int n_qtiles = (a.N + kDqBR - 1) / kDqBR;
+  SparseArgs sp;
+  if constexpr (SPARSE) sp = SparseArgs{a.mask, a.H, a.mask_heads, a.block_q, a.block_k};
   if (stages & kStagePre) {
     constexpr int RPB = 256 / (D / (16 / (int)sizeof(T)));
     const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
@@ -960,42 +1119,43 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   }
   if (stages & kStageDkDv) {
     if constexpr (sizeof(T) == 2) {
-      hipLaunchKernelGGL((fa_bwd_dkdv_bf16_kernel<D, CAUSAL, DROP>), dim3(n_ktiles * BH), dim3(kKvThreads), 0,
-                         stream, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+      hipLaunchKernelGGL((fa_bwd_dkdv_bf16_kernel<D, CAUSAL, SPARSE, DROP>), dim3(n_ktiles * BH), dim3(kKvThreads),
+                         0, stream, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                          static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.dsum, a.nlse,
                          static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, BH, n_ktiles,
-                         wg_group(n_ktiles, 32), a.scale, a.drop);   // 1 workgroup per CU
+                         wg_group(n_ktiles, 32), a.scale, sp, a.drop);   // 1 workgroup per CU
     } else {
       using C = BwdCfg<T, D>;
-      auto kern = fa_bwd_dkdv_kernel<T, D, CAUSAL, DROP>;
+      constexpr int bytes = C::BYTES + (SPARSE ? list_bytes(kBwdListCap) : 0);
+      auto kern = fa_bwd_dkdv_kernel<T, D, CAUSAL, SPARSE, DROP>;
       static const hipError_t attr_err =
-          hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::BYTES);
+          hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
       if (attr_err != hipSuccess) return attr_err;
-      hipLaunchKernelGGL(kern, dim3(n_ktiles * BH), dim3(kBwdThreads), C::BYTES, stream,
+      hipLaunchKernelGGL(kern, dim3(n_ktiles * BH), dim3(kBwdThreads), bytes, stream,
                          static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                          static_cast<const T*>(a.dout), a.dsum, a.nlse, static_cast<T*>(a.dk),
-                         static_cast<T*>(a.dv), a.N, BH, n_ktiles, wg_group(n_ktiles, 32), a.scale, a.drop);
+                         static_cast<T*>(a.dv), a.N, BH, n_ktiles, wg_group(n_ktiles, 32), a.scale, sp, a.drop);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & kStageDq) {
     if constexpr (sizeof(T) == 2) {
-      hipLaunchKernelGGL((fa_bwd_dq_bf16_kernel<D, CAUSAL, DROP>), dim3(n_qtiles * BH), dim3(kDqThreads), 0,
+      hipLaunchKernelGGL((fa_bwd_dq_bf16_kernel<D, CAUSAL, SPARSE, DROP>), dim3(n_qtiles * BH), dim3(kDqThreads), 0,
                          stream, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                          static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.dsum, a.nlse,
                          static_cast<bf16*>(a.dq), a.N, BH, n_qtiles,
-                         wg_group(n_qtiles, 64), a.scale, a.drop);   // 2 workgroups per CU
+                         wg_group(n_qtiles, 64), a.scale, sp, a.drop);   // 2 workgroups per CU
     } else {
-      constexpr int bytes = 4 * kDqBC * D * (int)sizeof(T);
-      auto kern = fa_bwd_dq_kernel<T, D, CAUSAL, DROP>;
+      constexpr int bytes = 4 * kDqBC * D * (int)sizeof(T) + (SPARSE ? kListBytes : 0);
+      auto kern = fa_bwd_dq_kernel<T, D, CAUSAL, SPARSE, DROP>;
       static const hipError_t attr_err =
           hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
       if (attr_err != hipSuccess) return attr_err;
       hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(kDqThreads), bytes, stream, static_cast<const T*>(a.q),
                          static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<const T*>(a.dout),
                          a.dsum, a.nlse, static_cast<T*>(a.dq), a.N, BH, n_qtiles, wg_group(n_qtiles, 32),
-                         a.scale, a.drop);
+                         a.scale, sp, a.drop);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1005,10 +1165,17 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
 
 }  // namespace
 
+// Instantiations: dense (with and without dropout) and block-sparse (no dropout).
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_bwd_c(const BwdArgs& a, int stages, hipStream_t s) {
+  if (a.mask) return launch_bwd_t<T, D, CAUSAL, true, false>(a, stages, s);
+  if (a.drop.on) return launch_bwd_t<T, D, CAUSAL, false, true>(a, stages, s);
+  return launch_bwd_t<T, D, CAUSAL, false, false>(a, stages, s);
+}
+
 template <typename T, int D>
 hipError_t launch_bwd_d(const BwdArgs& a, int stages, hipStream_t s) {
-  if (a.causal) return a.drop.on ? launch_bwd_t<T, D, true, true>(a, stages, s) : launch_bwd_t<T, D, true, false>(a, stages, s);
-  return a.drop.on ? launch_bwd_t<T, D, false, true>(a, stages, s) : launch_bwd_t<T, D, false, false>(a, stages, s);
+  return a.causal ? launch_bwd_c<T, D, true>(a, stages, s) : launch_bwd_c<T, D, false>(a, stages, s);
 }
 
 hipError_t launch_backward(const BwdArgs& a, int stages, hipStream_t s) {

@@ -291,6 +291,72 @@ inline int wg_group(int n_tiles, int slots_per_xcd) {
   return fit > 4 ? fit : 4;
 }
 
+// ---------------------------------------------------------------- block-sparse tile lists
+// Block-sparse attention ("Overview of Flash Attention series", Block-sparse
+// Flashattention) visits only the tiles a block mask keeps.  Each workgroup
+// lists its tiles in LDS, in increasing order: act[i] = tile index,
+// wbit[i] = which of its waves compute that tile (bit w; at most 8 waves).
+// The mask is uint8 [mask_heads][ceil(N/block_q)][ceil(N/block_k)], non-zero
+// keeps a block; mask_heads = 1 shares one mask, otherwise head h of every
+// batch uses mask h.
+typedef __attribute__((address_space(3))) unsigned short lds_u16;
+typedef __attribute__((address_space(3))) int lds_i32;
+// A list of up to CAP entries takes list_bytes(CAP) bytes of LDS: act (u16),
+// wbit (u8), then 8 per-wave counters.  CAP = kListMax covers N <= 65536 in
+// tiles of 64; lists of 32-row blocks take 2 * kListMax.
+constexpr int kListMax = 1024;
+constexpr int list_bytes(int cap) { return (3 * cap + 8 * 4 + 255) / 256 * 256; }
+constexpr int kListBytes = list_bytes(kListMax);
+
+struct TileList {
+  lds_u16* act;
+  lds_u8* wbit;
+  lds_i32* cnt;
+};
+template <int CAP = kListMax>
+__device__ __forceinline__ TileList tile_list_at(lds_u8* base) {
+  return {(lds_u16*)base, base + 2 * CAP, (lds_i32*)(base + 3 * CAP)};
+}
+// The mask as the kernels take it (mask == nullptr: dense).
+struct SparseArgs {
+  const unsigned char* mask = nullptr;
+  int H = 1, mask_heads = 1, block_q = 32, block_k = 64;
+};
+// This head's mask rows (each ceil(N/block_k) entries).
+__device__ __forceinline__ const unsigned char* mask_of_head(const unsigned char* mask, int bh, int H, int mask_heads,
+                                                             int tq_n, int tk_n) {
+  return mask + (size_t)(mask_heads > 1 ? bh % H : 0) * tq_n * tk_n;
+}
+// Lists the tiles j in [0, n) with bits_of(j) != 0; every thread of the NW
+// waves calls it.  Returns the number of listed tiles.
+template <int NW, typename BitsFn>
+__device__ int build_tile_list(int n, BitsFn bits_of, const TileList& tl, int tid, int w, int lane) {
+  constexpr int NT = NW * 64;
+  int n_act = 0;
+  for (int base = 0; base < n; base += NT) {
+    const int j = base + tid;
+    const unsigned bits = j < n ? bits_of(j) : 0u;
+    const unsigned long long bal = __builtin_amdgcn_ballot_w64(bits != 0);
+    if (lane == 0) tl.cnt[w] = __builtin_popcountll(bal);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+      const int c = tl.cnt[w2];
+      off += w2 < w ? c : 0;
+      tot += c;
+    }
+    if (bits) {
+      const int pos = n_act + off + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+      tl.act[pos] = (unsigned short)j;
+      tl.wbit[pos] = (unsigned char)bits;
+    }
+    n_act += tot;
+    __syncthreads();
+  }
+  return n_act;
+}
+
 // ---------------------------------------------------------------- dropout
 // The dropout mask is never stored: every kernel regenerates the bits it
 // needs from the counter-based generator Philox4x32-10 (Salmon, Moraes,

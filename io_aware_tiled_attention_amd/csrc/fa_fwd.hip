@@ -48,10 +48,8 @@ constexpr int kFwdQW = 32;                      // query rows per wave
 constexpr int kFwdBR = kFwdWaves * kFwdQW;      // query rows per workgroup
 constexpr int kFwdBC = 64;                      // keys per K/V tile
 constexpr int kFwdThreads = kFwdWaves * 64;
-// Block-sparse: the key tiles a workgroup visits are listed in LDS, at most
-// this many (N <= 64 * kFwdMaxTiles = 65536), with one bit per wave.
-constexpr int kFwdMaxTiles = 1024;
-constexpr int kFwdListBytes = 4096;   // u16 tile index + u8 wave bits per entry, 4 counters
+// Block-sparse: the key tiles a workgroup visits are listed in LDS (TileList,
+// N <= 64 * kListMax = 65536), with one bit per wave.
 
 template <typename T, int D>
 struct FwdSmem {
@@ -146,47 +144,26 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   // The tiles this workgroup visits, in order: every tile up to kv_end
   // (dense), or the listed ones (block-sparse).  tile_of(i) is the i-th
   // visited tile, active(i) whether this wave computes it.
-  typedef __attribute__((address_space(3))) unsigned short lds_u16;
-  typedef __attribute__((address_space(3))) int lds_i32;
-  lds_u16* act = (lds_u16*)(smem + L::BYTES);
-  lds_u8* wbit = (lds_u8*)(act + kFwdMaxTiles);
+  const TileList tl = tile_list_at(smem + L::BYTES);
   int n_act = ntiles;
   if constexpr (SPARSE) {
-    lds_i32* cnt = (lds_i32*)(wbit + kFwdMaxTiles);
     const int tk_n = (N + block_k - 1) / block_k;
     const int tq_n = (N + block_q - 1) / block_q;
-    const unsigned char* mrow = mask + (size_t)(mask_heads > 1 ? bh % H : 0) * tq_n * tk_n;
-    n_act = 0;
-    for (int base = 0; base < ntiles; base += kFwdThreads) {
-      const int j = base + tid;
-      unsigned bits = 0;
-      if (j < ntiles) {
-        const int kb = j * kFwdBC / block_k;
+    const unsigned char* mrow = mask_of_head(mask, bh, H, mask_heads, tq_n, tk_n);
+    n_act = build_tile_list<kFwdWaves>(
+        ntiles,
+        [&](int j) -> unsigned {
+          const int kb = j * kFwdBC / block_k;
+          unsigned bits = 0;
 #pragma unroll
-        for (int w2 = 0; w2 < kFwdWaves; ++w2) {
-          const int qw = q0 + w2 * kFwdQW;
-          const bool reach = qw < N && !(CAUSAL && j * kFwdBC > qw + kFwdQW - 1);
-          if (reach && mrow[(qw / block_q) * tk_n + kb] != 0) bits |= 1u << w2;
-        }
-      }
-      const unsigned long long bal = __builtin_amdgcn_ballot_w64(bits != 0);
-      if (lane == 0) cnt[w] = __builtin_popcountll(bal);
-      __syncthreads();
-      int off = 0, tot = 0;
-#pragma unroll
-      for (int w2 = 0; w2 < kFwdWaves; ++w2) {
-        const int c = cnt[w2];
-        off += w2 < w ? c : 0;
-        tot += c;
-      }
-      if (bits) {
-        const int pos = n_act + off + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
-        act[pos] = (unsigned short)j;
-        wbit[pos] = (unsigned char)bits;
-      }
-      n_act += tot;
-      __syncthreads();
-    }
+          for (int w2 = 0; w2 < kFwdWaves; ++w2) {
+            const int qw = q0 + w2 * kFwdQW;
+            const bool reach = qw < N && !(CAUSAL && j * kFwdBC > qw + kFwdQW - 1);
+            if (reach && mrow[(qw / block_q) * tk_n + kb] != 0) bits |= 1u << w2;
+          }
+          return bits;
+        },
+        tl, tid, w, lane);
   } else {
     (void)mask;
     (void)H;
@@ -195,11 +172,11 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     (void)block_k;
   }
   auto tile_of = [&](int i) -> int {
-    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)act[i]);
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)tl.act[i]);
     else return i;
   };
   auto active = [&](int i) -> bool {
-    if constexpr (SPARSE) return (__builtin_amdgcn_readfirstlane((int)wbit[i]) >> w) & 1;
+    if constexpr (SPARSE) return (__builtin_amdgcn_readfirstlane((int)tl.wbit[i]) >> w) & 1;
     else return i <= wave_last;
   };
 
@@ -323,7 +300,7 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   using L = FwdSmem<T, D>;
-  constexpr int bytes = L::BYTES + (SPARSE ? kFwdListBytes : 0);
+  constexpr int bytes = L::BYTES + (SPARSE ? kListBytes : 0);
   auto kern = fa_fwd_kernel<T, D, CAUSAL, SPARSE, DROP>;
   // raise the dynamic-LDS limit once per instantiation (thread-safe static init)
   static const hipError_t attr_err =

@@ -33,7 +33,7 @@ struct FwdArgs {
   DropParams drop{};
 };
 
-constexpr int kSparseMaxN = 65536;   // N limit of the block-sparse forward
+constexpr int kSparseMaxN = 65536;   // N limit of block-sparse attention (tile lists in LDS)
 
 struct BwdArgs {
   const void* q;
@@ -50,6 +50,9 @@ struct BwdArgs {
   float* dsum;     // [B*H*N]   D_i = do_i . o_i          (workspace)
   float* nlse;     // [B*H*N]   -lse_i, exponent domain   (workspace)
   DropParams drop{};
+  // block-sparse backward only (mask == nullptr: dense)
+  const unsigned char* mask = nullptr;
+  int mask_heads = 0, block_q = 0, block_k = 0;
 };
 
 // Forward with OCP E4M3 inputs (one byte per element) and bf16 output.

@@ -173,6 +173,33 @@ def test_block_sparse_forward_empty_problem_is_a_noop(kw):
     assert fwd_sparse(**kw) == 0
 
 
+def bwd_sparse(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, mask=FAKE, mask_heads=1,
+             block_q=128, block_k=64, B=1, H=2, N=1024, d=128, causal=1, scale=0.125, dtype=_lib.FA_BF16,
+             ws=0x100000, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return fa.fa_backward_block_sparse(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                       a["mask"], a["mask_heads"], a["block_q"], a["block_k"], a["B"], a["H"],
+                                       a["N"], a["d"], a["causal"], a["scale"], a["dtype"], a["ws"], a["ws_bytes"],
+                                       a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mask=0), 1), (dict(q=0), 1), (dict(do=0), 1), (dict(lse=0), 1), (dict(dk=0), 1), (dict(dq=0), 1),
+    (dict(N=-1), 2), (dict(d=96), 3), (dict(dtype=3), 4), (dict(scale=float("inf")), 5),
+    (dict(block_q=0), 9), (dict(block_q=48), 9), (dict(block_k=32), 9), (dict(block_k=96), 9),
+    (dict(mask_heads=0), 9), (dict(mask_heads=3), 9), (dict(N=65536 + 64), 9),
+    (dict(ws=0), 6), (dict(ws_bytes=16), 6), (dict(ws=0x100000 + 64), 8), (dict(dv=FAKE + 4), 8),
+])
+def test_block_sparse_backward_rejects_invalid_arguments(kw, status):
+    assert bwd_sparse(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0, mask=0, q=0, ws=0), dict(H=0, mask_heads=1)])
+def test_block_sparse_backward_empty_problem_is_a_noop(kw):
+    assert bwd_sparse(**kw) == 0
+
+
 def test_block_sparse_accepts_per_head_masks_and_large_blocks_in_validation():
     # mask_heads = H and block sizes that are multiples (validation only; the call then fails at the
     # NULL pointer check that follows geometry)
