@@ -11,7 +11,8 @@ FLOP counting convention: forward 4*B*H*N^2*d, halved when causal; backward
 2.5x forward.  The value is total (forward + backward) FLOPs per step over
 the wall time of a step, in TFLOP/s.
 
-Besides the step, "extra" carries the 4K shape, the block-sparse (forward and
+Besides the step, "extra" carries the 4K shape, per-call timings (median,
+p10, p90) of the five parity configurations, the block-sparse (forward and
 backward), decoding,
 dropout and FP8 paths, and the library GEMM's rate on N(0,1) operands in the
 same run (the practical matrix-core ceiling for such data, with each kernel's
@@ -19,7 +20,7 @@ fraction of it).
 
 Prints ONE JSON line.  Options: --gpus N (only 1: the path runs on one GPU),
 --steps K, --warmup W, --no-cpu-baseline, --no-extra, --decode-only, --dropout-only,
---fp8-only, --sparse-only.
+--fp8-only, --sparse-only, --configs-only.
 """
 from __future__ import annotations
 
@@ -419,6 +420,66 @@ def gemm_ceiling_measurement(torch, dev, steps, n=16384):
     return out
 
 
+CONFIG_NAMES = ["single_head_f32", "gpt2_small_bf16", "causal_4k_d128", "causal_16k_d128", "causal_bwd_4k_d64"]
+
+
+def config_measurement(fa, torch, dev, warm=10, timed=50):
+    """Per-call timing of each of the five parity configurations: `warm`
+    untimed calls, then `timed` calls each bracketed by its own pair of HIP
+    events on the launch stream; median, p10 and p90 in ms and TFLOP/s at the
+    median (forward; the backward problem: its three-stage backward, with O and
+    lse from the forward on the same inputs).  GPU only; the CPU oracle's
+    per-head rate for the same passes is part of the cpu_baseline leg."""
+    import numpy as np
+    from workloads import PROBLEMS, make_inputs
+    raw = fa.load_library()
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for name in CONFIG_NAMES:
+        p = PROBLEMS[name]
+        inputs = make_inputs(p)
+        q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
+        dt = 0 if p.dtype == "f32" else 1
+        o = torch.empty_like(q)
+        lse = torch.empty((p.B, p.H, p.N), dtype=torch.float32, device=dev)
+
+        def fwd():
+            st = raw.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), p.B, p.H,
+                                p.N, p.d, int(p.causal), p.scale, dt, stream)
+            assert st == 0, st
+        fn, flops, what = fwd, p.fwd_flops(), "forward"
+        if p.backward:
+            do = inputs["do"].to(dev)
+            dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+            ws_n = raw.fa_backward_workspace_size(p.B, p.H, p.N, p.d)
+            ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+            fwd()
+
+            def bwd():
+                st = raw.fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), p.B, p.H, p.N, p.d,
+                                     int(p.causal), p.scale, dt, ws.data_ptr(), ws_n, stream)
+                assert st == 0, st
+            fn, flops, what = bwd, p.bwd_flops(), "backward"
+        for _ in range(warm):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(timed)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+        med, p10, p90 = (float(np.percentile(ms, x)) for x in (50, 10, 90))
+        out[name] = {"pass": what, "B": p.B, "H": p.H, "N": p.N, "d": p.d, "dtype": p.dtype, "causal": p.causal,
+                     "calls": timed, "median_ms": med, "p10_ms": p10, "p90_ms": p90,
+                     "tflops_at_median": flops / med * 1e-9, "frac_peak": flops / med * 1e-9 / PEAK_BF16_TFLOPS}
+        del q, k, v, o, lse, inputs
+        torch.cuda.empty_cache()
+    return out
+
+
 DECODE_SHAPES = [(1, 32, 1, 65536), (8, 32, 1, 8192)]    # (B, H, Nq, Nk), d = 128, bf16, causal
 
 
@@ -497,6 +558,30 @@ def cpu_baseline(inputs, p, heads):
                       f"{os.cpu_count()} logical cpus); FLOPs counted with the same convention as the GPU"}
 
 
+def cpu_config_heads():
+    """The fp64 oracle on one head of each parity configuration (the same pass
+    as config_measurement): seconds and the per-head rate."""
+    import torch
+    from oracle import attention_ref as ref
+    from workloads import PROBLEMS, make_inputs
+    out = {}
+    for name in CONFIG_NAMES:
+        p = PROBLEMS[name]
+        inputs = make_inputs(p)
+        qh, kh, vh = (inputs[n][0, 0].to(torch.float64).numpy() for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        if p.backward:
+            ref.backward_head(qh, kh, vh, inputs["do"][0, 0].to(torch.float64).numpy(), p.causal, p.scale)
+            flops = p.bwd_flops()
+        else:
+            ref.forward_head(qh, kh, vh, p.causal, p.scale)
+            flops = p.fwd_flops()
+        sec = time.perf_counter() - t0
+        out[name] = {"pass": "backward" if p.backward else "forward", "heads": 1, "seconds": sec,
+                     "tflops": flops / (p.B * p.H) / sec * 1e-12}
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -510,6 +595,8 @@ def main(argv=None):
                          "split-KV decoding, dropout, FP8 forward)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the split-KV decoding measurement (one JSON line; for kernel traces)")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="only the per-call timing of the five parity configurations (one JSON line)")
     ap.add_argument("--sparse-only", action="store_true",
                     help="only the block-sparse forward and backward measurement (one JSON line)")
     ap.add_argument("--fp8-only", action="store_true",
@@ -547,6 +634,9 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": {"bytes_read_per_copy": 4 * n, "bytes_written_per_copy": 4 * n,
                                                "copies": 3}}), flush=True)
+        return 0
+    if args.configs_only:
+        print(json.dumps({"configs": config_measurement(fa, torch, dev)}), flush=True)
         return 0
     if args.sparse_only:
         print(json.dumps({"block_sparse_16k_d128": sparse_measurement(fa, torch, dev, max(3, args.steps))}), flush=True)
@@ -597,6 +687,8 @@ def main(argv=None):
         torch.cuda.empty_cache()
         extra["fp8_16k_d128"] = fp8_measurement(fa, torch, dev, max(5, args.steps // 2))
         torch.cuda.empty_cache()
+        extra["configs"] = config_measurement(fa, torch, dev)
+        torch.cuda.empty_cache()
         ceil = gemm_ceiling_measurement(torch, dev, 5)
         g16 = ceil["bf16_tflops"]
         ceil["frac_of_bf16_gemm"] = {"fwd": kt["fwd"]["tflops"] / g16, "bwd_dkdv": kt["bwd_dkdv"]["tflops"] / g16,
@@ -623,6 +715,8 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inputs, p, args.cpu_heads)
+        if not args.no_extra:
+            out["cpu_baseline"]["per_config_one_head"] = cpu_config_heads()
     print(json.dumps(out), flush=True)
     return 0
 
