@@ -31,7 +31,10 @@
  *     attention); it must be finite and >= 0.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *     asynchronously; results are valid once the caller synchronises the
- *     stream.
+ *     stream.  The calls enqueue kernels only (no allocation, memset, copy or
+ *     synchronisation), so they can be captured into a HIP graph and
+ *     replayed; make the first call of each kind outside a capture (it sets
+ *     a kernel's LDS limit once per process).
  *   - Outputs must not alias inputs.
  *   - B, H or N equal to 0 describes an empty problem: the call validates the
  *     pointers it can, enqueues nothing and returns FA_OK.
