@@ -124,3 +124,62 @@ def test_block_sparse_backward_rejects_bad_geometry_before_launch():
         mask = torch.ones(shape, dtype=torch.uint8, device=dev)
         with pytest.raises(fa.FaError, match="FA_ERR_MASK"):
             fa.backward_block_sparse(q, k, v, q, do, lse, mask, bq, bk)
+
+
+@pytest.mark.parametrize("dtype,d,bq,bk", [("bf16", 128, 64, 64), ("f32", 64, 32, 64)])
+def test_block_sparse_full_tile_lists_at_max_n(dtype, d, bq, bk):
+    """N = 65536, the largest block-sparse N: every query block keeps key block
+    0, and query block r keeps every key block.  Key tile 0's dK/dV workgroup
+    then lists every query block (1024 blocks of 64 rows in bf16, 2048 of 32 in
+    fp32) and query block r's forward and dQ workgroups list all 1024 key
+    tiles -- full lists.  The reference splits exactly by query rows: rows
+    outside block r attend keys 0..bk-1 only, rows of block r attend all keys;
+    gradients of K and V add over the two groups.
+
+    dO is drawn N(0, 0.2^2): here all 65536 rows send gradient to the same 64
+    keys, and with N(0, 1) their dK and dV reach 27 in magnitude, past the
+    range (|x| <~ 5) the bf16 bar was set for; there the bar is one output ulp
+    while the rounding of dS to bf16, summed over 65536 rows, alone reaches
+    about two (a reference that rounds dS likewise leaves only the output's
+    own rounding).  At 0.2 the gradients stay within that range."""
+    N, r = 65536, 300
+    announce(f"block-sparse full lists: {dtype} N={N} d={d} blocks {bq}x{bk}")
+    dev = torch.device("cuda", 0)
+    inputs = random_inputs(1, 1, N, d, dtype, seed=1970 + d, with_do=True)
+    inputs["do"] = (inputs["do"].float() * 0.2).to(inputs["do"].dtype)
+    mask = torch.zeros((1, N // bq, N // bk), dtype=torch.uint8)
+    mask[0, :, 0] = 1
+    mask[0, r, :] = 1
+    q, k, v, do = (inputs[n].to(dev) for n in ("q", "k", "v", "do"))
+    m = mask.to(dev)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = fa.forward_block_sparse(q, k, v, m, bq, bk, scale=scale)
+    dq, dk, dv = fa.backward_block_sparse(q, k, v, o, do, lse, m, bq, bk, scale=scale)
+    torch.cuda.synchronize()
+    o, lse, dq, dk, dv = (t[0, 0].cpu() for t in (o, lse, dq, dk, dv))
+
+    q64, k64, v64, do64 = (to64(inputs[n][0, 0]) for n in ("q", "k", "v", "do"))
+    rows_r = np.arange(r * bq, (r + 1) * bq)
+    rest = np.setdiff1d(np.arange(N), rows_r)
+    o_ref, lse_ref, dq_ref = np.zeros((N, d)), np.zeros(N), np.zeros((N, d))
+    dk_ref, dv_ref = np.zeros((N, d)), np.zeros((N, d))
+    # rows outside block r: dense attention over keys 0 .. bk-1
+    o_ref[rest], lse_ref[rest] = ref.forward_head(q64[rest], k64[:bk], v64[:bk], False, scale)
+    gq, gk, gv = ref.backward_head(q64[rest], k64[:bk], v64[:bk], do64[rest], False, scale)
+    dq_ref[rest] = gq
+    dk_ref[:bk] += gk
+    dv_ref[:bk] += gv
+    # rows of block r: dense attention over all keys
+    o_ref[rows_r], lse_ref[rows_r] = ref.forward_head(q64[rows_r], k64, v64, False, scale)
+    gq, gk, gv = ref.backward_head(q64[rows_r], k64, v64, do64[rows_r], False, scale)
+    dq_ref[rows_r] = gq
+    dk_ref += gk
+    dv_ref += gv
+
+    from gpu_helpers import TOL, TOL_LSE
+    bf = dtype == "bf16"
+    assert_close("O", o, o_ref, TOL[dtype], bf16_output=bf)
+    assert_close("lse", lse, lse_ref, TOL_LSE)
+    assert_close("dQ", dq, dq_ref, grad_tol(dtype, dq_ref), bf16_output=bf)
+    assert_close("dK", dk, dk_ref, grad_tol(dtype, dk_ref), bf16_output=bf)
+    assert_close("dV", dv, dv_ref, grad_tol(dtype, dv_ref), bf16_output=bf)
