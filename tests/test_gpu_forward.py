@@ -11,7 +11,8 @@ import io_aware_tiled_attention_amd as fa
 from workloads import PROBLEMS, make_inputs, random_inputs
 
 from gpu_helpers import (TOL, TOL_LSE, announce, assert_close, check_forward_full, check_forward_rows,
-                         gpu_forward, require_gpu, to64)
+                         gpu_backward, gpu_forward, grad_tol, require_gpu, to64)
+from oracle import attention_ref as ref
 
 pytestmark = pytest.mark.gpu
 
@@ -140,3 +141,25 @@ def test_stream_argument_is_honoured():
         o, l = fa.forward(q, k, v, causal=True)
     s.synchronize()
     assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
+def test_the_pages_numpy_exercise_shape_fp32():
+    """"Как работает FlashAttention математически", the NumPy exercise: one head,
+    n = 1024, d = 64, blocks of 128, the tiled result within 1e-5 of standard
+    attention, plus the backward by recomputation -- on the fp32 path.  The
+    exercise writes S = Q K^T without a scale and compares two float64 NumPy
+    computations (the oracle's test of the same name does that); in fp32 at
+    scale 1 the scores reach ~40 and each carries ~5e-6 relative rounding,
+    which alone puts O ~1e-5 off.  So the GPU runs the exercise's shape at the
+    library's scale 1/sqrt(d), where the 1e-5 bar on O applies."""
+    announce("the page's NumPy exercise shape: fp32 N=1024 d=64, forward and backward")
+    scale = 1.0 / math.sqrt(64)
+    inputs = random_inputs(1, 1, 1024, 64, "f32", seed=2200, with_do=True)
+    o, lse, dq, dk, dv = gpu_backward(inputs, False, scale)
+    q, k, v, do = (to64(inputs[n][0, 0]) for n in ("q", "k", "v", "do"))
+    o_r, lse_r = ref.forward_head(q, k, v, False, scale)
+    assert_close("O", o[0, 0], o_r, TOL["f32"])
+    assert_close("lse", lse[0, 0], lse_r, TOL_LSE)
+    dq_r, dk_r, dv_r = ref.backward_head(q, k, v, do, False, scale)
+    for name, got, want in (("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r)):
+        assert_close(name, got[0, 0], want, grad_tol("f32", want))

@@ -356,6 +356,28 @@ def test_pins_catch_planted_forward_mistakes(worked):
     assert not np.allclose(recurrence(-1), o_page, rtol=1e-6)
 
 
+def test_the_pages_numpy_exercise_tiled_equals_standard():
+    """"Как работает FlashAttention математически", the NumPy exercise: random
+    Q, K, V with n = 1024, d = 64, S = Q K^T (no scale), blocks of 128; the
+    tiled forward with the online-softmax correction must match standard
+    attention within 1e-5 (here, in fp64, far closer), in both forms of the
+    recurrence, and so must the backward by recomputation from m and l."""
+    n, d, blk = 1024, 64, 128
+    q, k, v, g = (_rand((n, d), 790 + i) for i in range(4))
+    o_std, lse_std = ref.forward_head(q, k, v, False, 1.0)
+    for form in ("deferred", "normalised"):
+        o_t, lse_t = ref.blockwise_forward_head(q, k, v, blk, blk, scale=1.0, form=form)
+        assert np.max(np.abs(o_t - o_std)) < 1e-5
+        np.testing.assert_allclose(o_t, o_std, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse_t, lse_std, rtol=1e-12)
+    # backward with recomputation: P rebuilt from the stored lse equals the one-shot P
+    dq, dk, dv = ref.backward_head(q, k, v, g, False, 1.0)
+    p_re = np.exp(ref.scores(q, k, 1.0, False) - lse_t[:, None])
+    p_std, _, _ = ref.softmax_stats(ref.scores(q, k, 1.0, False))
+    np.testing.assert_allclose(p_re, p_std, rtol=1e-9, atol=1e-15)
+    np.testing.assert_allclose(p_re.T @ g, dv, rtol=1e-9, atol=1e-12)
+
+
 # ---------------------------------------------------------------- block-sparse attention
 # "Overview of Flash Attention series", Block-sparse Flashattention: a mask
 # that is constant on blocks; zero blocks are skipped (no weight at all).
