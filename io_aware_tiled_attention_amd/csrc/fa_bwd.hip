@@ -15,15 +15,18 @@
 // Three launches on the caller's stream, none of them with atomics:
 //   1. fa_bwd_pre: D_i = rowsum(dO o O) in fp32 and -lse_i (in the exponent
 //      domain) into the workspace.
-//   2. fa_bwd_dkdv: a workgroup owns 128 keys (4 waves x 32) and keeps its
-//      slice of K, V and the fp32 accumulators dK^T, dV^T in registers while
-//      sweeping the query blocks that can see them (all blocks, or the blocks
-//      at or below the diagonal when causal), BQ query rows at a time through
-//      double-buffered LDS.  Per 32-row sub-block each wave recomputes S and P
-//      for its 32 keys, forms dP and dS, and accumulates dV^T += dO^T P and
-//      dK^T += Q^T dS on the matrix cores: P and dS are already in B-operand
-//      layout, dO^T and Q^T come from the row-major LDS tiles through the
-//      gfx950 transpose read.
+//   2. fa_bwd_dkdv: a workgroup owns 128 keys and keeps the fp32
+//      accumulators dK^T, dV^T of its keys in registers while sweeping the
+//      query blocks that can see them (all blocks, or the blocks at or below
+//      the diagonal when causal) through double-buffered LDS.  Per 32-row
+//      sub-block a wave recomputes S and P for its 32 keys, forms dP and dS,
+//      and accumulates dV^T += dO^T P and dK^T += Q^T dS on the matrix cores:
+//      P and dS are already in B-operand layout, dO^T and Q^T come from the
+//      row-major LDS tiles through the gfx950 transpose read.  bf16
+//      (fa_bwd_dkdv_bf16_kernel): 8 waves, K and V resident in LDS, the two
+//      waves of a SIMD taking the two 32-row halves of each 64-row block and
+//      summing their partials through LDS at the end.  fp32: 4 waves with K
+//      and V in registers.
 //   3. fa_bwd_dq: the same recomputation in the transposed orientation, one
 //      workgroup per 128 query rows (like the forward): S^T = K Q^T and
 //      dP^T = V dO^T leave each lane with one query's scores, lse and D are
@@ -34,6 +37,11 @@
 // needs no cross-workgroup reduction: on this GPU fp32 atomics are executed at
 // the memory side, and the fused form spent most of its time waiting on them.
 // The pages leave the backward loop order open (their figure is missing).
+// Every grid is launched in the XCD-aware order of wg_order (longest work
+// first within head groups).  SPARSE instantiations (block-sparse attention,
+// "Overview of Flash Attention series", Block-sparse Flashattention) visit
+// only the tiles a block mask keeps, from per-workgroup lists in LDS
+// (build_tile_list); DROP ones regenerate the forward's dropout mask.
 #include "fa_common.h"
 #include "fa_internal.h"
 

@@ -36,7 +36,8 @@
 //     gfx950 LDS transpose read (ds_read_b64_tr_b16);
 //   * causal: tiles entirely above a wave's diagonal are skipped, diagonal and
 //     ragged-tail tiles are masked (key > query or key >= N -> -inf).  Query
-//     tiles are launched longest-first.
+//     tiles are launched longest-first within XCD-aware head groups
+//     (wg_order).
 #include "fa_common.h"
 #include "fa_internal.h"
 
