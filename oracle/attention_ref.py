@@ -121,7 +121,9 @@ __all__ = [
     "philox4x32",
     "dropout_threshold",
     "dropout_keep_mask",
+    "dropout_keep_rows",
     "forward_dropout_head",
+    "forward_dropout_rows",
     "backward_dropout_head",
     "finite_difference_grads_dropout",
     "e4m3_decode",
@@ -680,7 +682,14 @@ def dropout_keep_mask(bh: int, n_q: int, n_k: int, seed: int, offset: int, t: in
     bytes numbered little-endian within the four output words; kept when
     that byte is >= t.
     """
-    rows = np.arange(n_q)
+    return dropout_keep_rows(bh, np.arange(n_q), n_k, seed, offset, t)
+
+
+def dropout_keep_rows(bh: int, rows, n_k: int, seed: int, offset: int, t: int) -> np.ndarray:
+    """The rows ``rows`` (query indices) of :func:`dropout_keep_mask`: [len(rows), n_k]
+    bool, the same definition evaluated only there (for sampled checks of long
+    sequences)."""
+    rows = np.asarray(rows, dtype=np.int64)
     cols = np.arange(n_k)
     qg = (rows // 4)[:, None]
     kg = (cols // 4)[None, :]
@@ -706,6 +715,23 @@ def forward_dropout_head(q, k, v, keep, t: int, causal: bool = False, scale: Opt
     rs = 256.0 / (256.0 - t)
     o = (p * keep * rs) @ v
     return o, m + np.log(l)
+
+
+def forward_dropout_rows(q, k, v, rows, keep_rows, t: int, causal: bool = False, scale: Optional[float] = None,
+                         q_selected: bool = False):
+    """:func:`forward_dropout_head` restricted to the query rows ``rows`` (the
+    row-wise definition, as :func:`forward_rows`); ``keep_rows`` are those rows
+    of the keep mask (:func:`dropout_keep_rows`).  Returns (O rows, lse rows)."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    rows = np.asarray(rows, dtype=np.int64)
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    s = scale * ((q if q_selected else q[rows]) @ k.T)
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] > rows[:, None], -np.inf, s)
+    p, m, l = softmax_stats(s)
+    rs = 256.0 / (256.0 - t)
+    return (p * keep_rows * rs) @ v, m + np.log(l)
 
 
 def backward_dropout_head(q, k, v, do, keep, t: int, causal: bool = False, scale: Optional[float] = None):

@@ -188,3 +188,28 @@ def test_dropout_2k_d128_sampled_heads():
     announce("dropout bf16 B=1 H=4 N=2048 d=128 causal p=0.1, two heads")
     inputs = random_inputs(1, 4, 2048, 128, "bf16", seed=33, with_do=True)
     check_dropout(inputs, True, 1 / math.sqrt(128), 0.1, seed=2024, offset=17, heads=[(0, 0), (0, 3)])
+
+
+@pytest.mark.slow
+def test_dropout_16k_bench_configuration_sampled_rows():
+    """The launch configuration the bench times: the 16K problem (B=1, H=32,
+    N=16384, d=128, causal, stressed K) with p = 0.1, seed 0x5EED, offset 0.
+    Sampled query rows of two heads, each against all of its keys, with the
+    keep mask regenerated for those rows by the oracle."""
+    from workloads import PROBLEMS, make_inputs
+    p = PROBLEMS["causal_16k_d128_bwd"]
+    announce("dropout bench configuration B=1 H=32 N=16384 d=128 causal p=0.1, sampled rows of heads 0 and 31")
+    inputs = make_inputs(p, with_do=True)
+    dev = torch.device("cuda", 0)
+    q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
+    o, lse = fa.forward(q, k, v, causal=True, scale=p.scale, dropout_p=0.1, seed=0x5EED, offset=0)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    t = ref.dropout_threshold(0.1)
+    rows = np.array([0, 1, 3, 777, 4096, 9999, 16380, 16383])
+    for h in (0, 31):
+        keep = ref.dropout_keep_rows(h, rows, p.N, 0x5EED, 0, t)
+        qh, kh, vh = (to64(inputs[n][0, h]) for n in ("q", "k", "v"))
+        o_r, lse_r = ref.forward_dropout_rows(qh[rows], kh, vh, rows, keep, t, True, p.scale, q_selected=True)
+        assert_close(f"O[0,{h}] rows", o[0, h][torch.as_tensor(rows)], o_r, TOL["bf16"], bf16_output=True)
+        assert_close(f"lse[0,{h}] rows", lse[0, h][torch.as_tensor(rows)], lse_r, TOL_LSE)

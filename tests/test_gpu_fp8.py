@@ -122,3 +122,17 @@ def test_fp8_4k_d128_sampled_heads():
     announce("fp8 B=1 H=8 N=4096 d=128 causal, two heads")
     inputs = fp8_inputs(1, 8, 4096, 128, seed=3100)
     check_bound(inputs, True, 1.0 / math.sqrt(128), (1.0, 1.0, 1.0), heads=[(0, 0), (0, 7)])
+
+
+@pytest.mark.slow
+def test_fp8_16k_bench_configuration_sampled_heads():
+    """The launch configuration the bench times: B=1, H=32, N=16384, d=128,
+    causal, the 16K problem's inputs (N(0,1)*0.5 with 1% of K rows x8) rounded
+    once to E4M3, descale 1.  Two whole heads against the oracle's bound."""
+    from workloads import PROBLEMS, make_inputs
+    p = PROBLEMS["causal_16k_d128"]
+    announce("fp8 bench configuration B=1 H=32 N=16384 d=128 causal, heads 5 and 31")
+    inp = make_inputs(p)
+    inputs = {n: inp[n].float().to(F8).view(torch.uint8).contiguous() for n in ("q", "k", "v")}
+    del inp
+    check_bound(inputs, True, p.scale, (1.0, 1.0, 1.0), heads=[(0, 5), (0, 31)])

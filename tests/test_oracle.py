@@ -569,6 +569,22 @@ def test_block_sparse_backward_pins_catch_planted_mistakes():
         np.testing.assert_allclose(a, b, rtol=0, atol=1e-7)
 
 
+def test_dropout_rows_are_rows_of_the_whole_head():
+    """The row-restricted mask and forward used for long-sequence samples agree
+    with the whole-head definitions on the rows they cover."""
+    n, d, t = 37, 5, 51
+    q, k, v = (_rand((n, d), 795 + i) for i in range(3))
+    rows = np.array([0, 3, 4, 17, 36])
+    full = ref.dropout_keep_mask(9, n, n, 0xABCDEF1234, 3, t)
+    part = ref.dropout_keep_rows(9, rows, n, 0xABCDEF1234, 3, t)
+    assert np.array_equal(part, full[rows])
+    for causal in (False, True):
+        o, lse = ref.forward_dropout_head(q, k, v, full, t, causal, 0.5)
+        o_r, lse_r = ref.forward_dropout_rows(q, k, v, rows, part, t, causal, 0.5)
+        np.testing.assert_allclose(o_r, o[rows], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse_r, lse[rows], rtol=1e-13)
+
+
 # ---------------------------------------------------------------- decoding (split-KV)
 # "Как работает FlashAttention математически" section 9 (FlashDecoding) and the
 # merge of key-block partials from "Overview of Flash Attention series", Tiling.
