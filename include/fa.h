@@ -61,7 +61,8 @@ enum fa_dtype {
 enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,      /* a required pointer is NULL (non-empty problem) */
-  FA_ERR_SHAPE = 2,     /* B, H or N negative, or one head's (N + 256) * d elements exceed 2^31 - 1 bytes */
+  FA_ERR_SHAPE = 2,     /* B, H or N negative; one head's (N + 256) * d elements exceed 2^31 - 1 bytes; or
+                           B * H * ceil(N / 128) is 2^23 or more (a launch's work items must fit in 32 bits) */
   FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 */
   FA_ERR_DTYPE = 4,     /* dtype is not an fa_dtype */
   FA_ERR_SCALE = 5,     /* scale is NaN, infinite or negative (FP8 descale factors: not finite or <= 0) */
@@ -127,8 +128,9 @@ int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o
  * NULL allowed, when one chunk per head is used), 256-byte aligned; contents
  * on entry are ignored, on exit unspecified.  Calls that run concurrently
  * must not share a workspace.
- * Shape errors (Nq > 32, Nk < 1, causal with Nq > Nk, num_splits < 0)
- * return FA_ERR_SHAPE.  Everything else as fa_forward.
+ * Shape errors (Nq > 32, Nk < 1, causal with Nq > Nk, num_splits < 0, or
+ * B * H * max(chunks, Nq) of 2^26 or more, past the grids' 32-bit work-item
+ * limit) return FA_ERR_SHAPE.  Everything else as fa_forward.
  */
 size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits);
 /* The number of key chunks fa_decode uses for these sizes (0 for invalid sizes). */

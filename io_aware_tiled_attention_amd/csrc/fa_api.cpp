@@ -13,6 +13,11 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Threads per workgroup: the largest of the per-tile kernels (the 8-wave bf16
+// dK/dV), and the decoding kernels'.
+constexpr int64_t kMaxTileThreads = 512;
+constexpr int64_t kDecodeThreads = 64;
+
 // Shape check shared by every entry point; `empty` is set for B*H*N == 0.
 int check_shape(int B, int H, int N, int d, int dtype, float scale, bool* empty) {
   if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
@@ -22,13 +27,15 @@ int check_shape(int B, int H, int N, int d, int dtype, float scale, bool* empty)
   // Sizes must fit the kernels' index arithmetic: rows and per-head byte
   // offsets use 32-bit ints, whole-tensor offsets 64-bit.  A ragged last
   // tile addresses up to kRowSlack rows past N (reads there are dropped by
-  // the buffer range check), so those rows must fit too.
+  // the buffer range check), so those rows must fit too.  A launch's
+  // work-item count (workgroups x threads) must fit in 32 bits: the largest
+  // per-tile grid has one workgroup of kMaxTileThreads per 128 rows of a head
+  // (the backward preprocess strides over its rows and has no such limit).
   constexpr int64_t kRowSlack = 256;
   const int64_t rows = (int64_t)B * H * N;
-  const int64_t tiles = ((int64_t)N + 127) / 128 * B * H;   // workgroups of the largest grid
+  const int64_t tiles = ((int64_t)N + 127) / 128 * B * H;
   const int64_t head_bytes = ((int64_t)N + kRowSlack) * d * (dtype == FA_BF16 ? 2 : 4);
-  if ((int64_t)B * H > INT32_MAX || head_bytes > INT32_MAX || tiles > INT32_MAX ||
-      rows > ((int64_t)1 << 40))
+  if ((int64_t)B * H > INT32_MAX || head_bytes > INT32_MAX || tiles * kMaxTileThreads > (int64_t)UINT32_MAX)
     return FA_ERR_SHAPE;
   *empty = rows == 0;
   return FA_OK;
@@ -205,6 +212,13 @@ static int check_decode(int B, int H, int Nq, int Nk, int d, int causal, int dty
   return FA_OK;
 }
 
+// The two decoding grids, B*H*splits and B*H*Nq workgroups of kDecodeThreads,
+// must each stay within 32-bit work-item counts.
+static bool decode_grids_fit(int B, int H, int Nq, int splits) {
+  const int64_t most = splits > Nq ? splits : Nq;
+  return (int64_t)B * H * most * kDecodeThreads <= (int64_t)UINT32_MAX;
+}
+
 // Decode workspace: partial O [B*H*S*Nq][d] fp32, then partial lse
 // [B*H*S*Nq] fp32, each region 256-byte aligned.  One chunk per head (S = 1)
 // writes the outputs directly and needs none.
@@ -217,7 +231,9 @@ static size_t decode_ws_bytes(int B, int H, int Nq, int d, int splits) {
 size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits) {
   bool empty = false;
   if (num_splits < 0 || check_decode(B, H, Nq, Nk, d, 0, FA_BF16, 1.f, &empty) != FA_OK || empty) return 0;
-  return decode_ws_bytes(B, H, Nq, d, fa::decode_splits(B, H, Nk, num_splits));
+  const int splits = fa::decode_splits(B, H, Nk, num_splits);
+  if (!decode_grids_fit(B, H, Nq, splits)) return 0;
+  return decode_ws_bytes(B, H, Nq, d, splits);
 }
 
 int fa_decode_num_splits(int B, int H, int Nk, int num_splits) {
@@ -233,10 +249,10 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
   if (st != FA_OK) return st;
   if (num_splits < 0) return FA_ERR_SHAPE;
   if (empty) return FA_OK;
+  const int splits = fa::decode_splits(B, H, Nk, num_splits);
+  if (!decode_grids_fit(B, H, Nq, splits)) return FA_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
-  const int splits = fa::decode_splits(B, H, Nk, num_splits);
-  if ((int64_t)B * H * splits > INT32_MAX) return FA_ERR_SHAPE;
   const size_t need = decode_ws_bytes(B, H, Nq, d, splits);
   fa::DecArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, causal ? 1 : 0, dtype, splits, scale, nullptr, nullptr};
   if (need > 0) {

@@ -73,7 +73,10 @@ struct BwdCfg {
 // ---------------------------------------------------------------- 1. preprocess
 // Row statistics in the workspace: dsum[i] = D_i = do_i . o_i, and
 // nlse[i] = -lse_i in the exponent domain of T, so that the later kernels
-// form P = ex(s * factor + nlse) with one FMA.
+// form P = ex(s * factor + nlse) with one FMA.  Blocks of RPB rows; the grid
+// is capped at kPreMaxBlocks and strides over the rest (a launch's work-item
+// count must fit in 32 bits).
+constexpr unsigned kPreMaxBlocks = 1u << 16;
 template <typename T, int D>
 __global__ __launch_bounds__(256)
 void fa_bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, const float* __restrict__ LSE,
@@ -82,21 +85,23 @@ void fa_bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, const 
   constexpr int CPR = D / VE;                 // threads per row
   constexpr int RPB = 256 / CPR;              // rows per block
   const int tid = threadIdx.x;
-  const size_t row = (size_t)blockIdx.x * RPB + tid / CPR;
   const int col = (tid % CPR) * VE;
-  float part = 0.f;
-  if (row < rows) {
-    union { uint4 u; T t[VE]; } o, d;
-    o.u = *reinterpret_cast<const uint4*>(O + row * D + col);
-    d.u = *reinterpret_cast<const uint4*>(dO + row * D + col);
+  for (size_t blk = blockIdx.x; blk * RPB < rows; blk += gridDim.x) {   // block-uniform trip count
+    const size_t row = blk * RPB + tid / CPR;
+    float part = 0.f;
+    if (row < rows) {
+      union { uint4 u; T t[VE]; } o, d;
+      o.u = *reinterpret_cast<const uint4*>(O + row * D + col);
+      d.u = *reinterpret_cast<const uint4*>(dO + row * D + col);
 #pragma unroll
-    for (int e = 0; e < VE; ++e) part += (float)o.t[e] * (float)d.t[e];
-  }
+      for (int e = 0; e < VE; ++e) part += (float)o.t[e] * (float)d.t[e];
+    }
 #pragma unroll
-  for (int off = CPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
-  if (row < rows && tid % CPR == 0) {
-    dsum[row] = part;
-    nlse[row] = -ExpDomain<T>::from_lse(LSE[row]);
+    for (int off = CPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    if (row < rows && tid % CPR == 0) {
+      dsum[row] = part;
+      nlse[row] = -ExpDomain<T>::from_lse(LSE[row]);
+    }
   }
 }
 
@@ -1119,7 +1124,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   if constexpr (SPARSE) sp = SparseArgs{a.mask, a.H, a.mask_heads, a.block_q, a.block_k};
   if (stages & kStagePre) {
     constexpr int RPB = 256 / (D / (16 / (int)sizeof(T)));
-    const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
+    const size_t blocks = (rows + RPB - 1) / RPB;
+    const dim3 grid((unsigned)(blocks < kPreMaxBlocks ? blocks : kPreMaxBlocks));
     hipLaunchKernelGGL((fa_bwd_pre_kernel<T, D>), grid, dim3(256), 0, stream, static_cast<const T*>(a.o),
                        static_cast<const T*>(a.dout), a.lse, a.dsum, a.nlse, rows);
     hipError_t e = hipGetLastError();

@@ -225,6 +225,21 @@ def test_per_head_limit_boundary_includes_the_ragged_tile_slack(d, dtype, elt):
     assert bwd(N=n_max + 1, d=d, dtype=dtype) == 2
 
 
+@pytest.mark.parametrize("N", [1, 128, 200, 4096])
+def test_launch_work_item_limit(N):
+    # A launch's work items (workgroups x threads) must fit in 32 bits; the
+    # largest per-tile grid is one 512-thread workgroup per 128 rows of a head,
+    # so B * H * ceil(N / 128) must stay below 2^23.  At N = 1 that is reachable
+    # with small tensors (2^23 heads of one row), so it is checked, not assumed.
+    tiles_per_head = -(-N // 128)
+    heads_max = (2**23 - 1) // tiles_per_head
+    assert fwd(B=1, H=heads_max, N=N, d=64, q=0) == 1        # accepted: fails at the NULL check next
+    assert fwd(B=1, H=heads_max + 1, N=N, d=64, q=0) == 2    # rejected as a shape error first
+    assert bwd(B=1, H=heads_max + 1, N=N, d=64) == 2
+    assert fa.fa_backward_workspace_size(1, heads_max + 1, N, 64) == 0
+    assert fa.fa_backward_workspace_size(1, heads_max, N, 64) > 0
+
+
 def dec(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, H=4, Nq=1, Nk=4096, d=128, causal=1, scale=0.125,
              dtype=_lib.FA_BF16, splits=0, ws=0x100000, ws_bytes=1 << 30, stream=None)
@@ -256,6 +271,18 @@ def test_decode_valid_shapes_pass_validation(kw):
 @pytest.mark.parametrize("kw", [dict(Nq=0), dict(B=0), dict(H=0), dict(Nq=0, Nk=0, q=0, k=0, ws=0)])
 def test_decode_empty_problem_is_a_noop(kw):
     assert dec(**kw) == 0
+
+
+def test_decode_grid_work_item_limit():
+    # both decoding grids (B*H*chunks and B*H*Nq workgroups of 64 threads) must
+    # stay below 2^32 work items, i.e. B * H * max(chunks, Nq) below 2^26
+    heads = 2**26 // 32                                  # Nq = 32: exactly 2^26 rows of the merge grid
+    assert dec(B=1, H=heads, Nq=32, Nk=64, splits=2, q=0) == 2
+    assert fa.fa_decode_workspace_size(1, heads, 32, 64, 128, 2) == 0
+    assert dec(B=1, H=heads - 1, Nq=32, Nk=64, splits=2, q=0) == 1     # accepted: NULL check next
+    assert fa.fa_decode_workspace_size(1, heads - 1, 32, 64, 128, 2) > 0
+    # the chunk grid cannot reach it first: chunks <= ceil(Nk / 32), and the
+    # cache's own shape check keeps B * H * ceil(Nk / 128) below 2^23
 
 
 def test_decode_split_count_and_workspace_size():

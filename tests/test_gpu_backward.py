@@ -121,3 +121,40 @@ def test_workspace_reuse_and_garbage_contents():
     dq2, dk2, dv2 = fa.backward(q, k, v, o, do, lse, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2) and torch.equal(dq1, dq2)
+
+
+@pytest.mark.parametrize("dtype,B,H,N,d", [("f32", 2, 3, 100003, 128), ("bf16", 1, 9, 250001, 64)])
+def test_preprocess_strides_over_more_rows_than_its_grid(dtype, B, H, N, d):
+    """The row statistics D_i = dO_i . O_i and -lse_i (in the exponent domain:
+    base 2 for bf16, base e for fp32) for more rows than one pass of the
+    preprocess grid covers (65536 blocks of 8 rows at fp32 d=128, of 32 rows at
+    bf16 d=64), with a ragged last block.  White box: the workspace holds D for
+    every row, then -lse, each region padded to 256 bytes; it starts as NaN so
+    that a row left unwritten shows."""
+    rows = B * H * N
+    announce(f"backward preprocess {dtype} rows={rows} d={d}")
+    dev = torch.device("cuda", 0)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    g = torch.Generator(device=dev).manual_seed(77)
+    o = torch.randn((B, H, N, d), generator=g, device=dev).to(tdt)
+    do = torch.randn((B, H, N, d), generator=g, device=dev).to(tdt)
+    lse = torch.randn((B, H, N), generator=g, device=dev) * 3.0
+    need = fa.workspace_size(B, H, N, d)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=dev)
+    code = fa._lib.FA_F32 if dtype == "f32" else fa._lib.FA_BF16
+    st = fa.fa_backward_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), B, H, N, d, code, ws.data_ptr(),
+                                   need, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    region = (rows * 4 + 255) // 256 * 256 // 4
+    dsum, nlse = ws[:rows], ws[region:region + rows]
+    prod = o.reshape(rows, d).double() * do.reshape(rows, d).double()
+    want = prod.sum(-1)
+    bound = 1e-5 * prod.abs().sum(-1) + 1e-30
+    err = (dsum.double() - want).abs()
+    assert bool(torch.isfinite(dsum).all()), "a row's D was not written"
+    assert bool((err <= bound).all()), f"D: worst err/bound {float((err / bound).max()):.3g}"
+    factor = 1.0 / math.log(2.0) if dtype == "bf16" else 1.0
+    want_n = -lse.reshape(rows).double() * factor
+    assert bool(torch.isfinite(nlse).all()), "a row's -lse was not written"
+    assert float((nlse.double() - want_n).abs().max()) <= 1e-6 * float(want_n.abs().max())
