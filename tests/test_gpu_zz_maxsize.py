@@ -19,6 +19,11 @@ seed (workloads.device_inputs).
   dQ is checked whole; O, lse, dK, dV on sampled rows.
 * Split-KV decoding of 32 new queries against a cache of that length, with the
   library's chunking and with one chunk, against the oracle's decode_head.
+* The largest grid the boundary accepts: B*H*ceil(N/128) = 2^23 - 1 one-row
+  heads, so every launch has its most workgroups (the backward's dK/dV grid
+  then holds 2^32 - 512 work items).  With one key per row P = 1 exactly, so
+  O = V and dV = dO bit for bit, lse = scale * q . k, and dS = 0 up to the
+  rounding of D, so dQ and dK vanish.
 
 Named to run last: together these take about two minutes.
 """
@@ -127,3 +132,33 @@ def test_decode_at_n_max(splits):
     o_ref, lse_ref = ref.decode_head(to64(qn[0, 0]), k64, v64, causal=True, scale=SHARP)
     assert_close("O", o[0, 0], o_ref, TOL["bf16"], bf16_output=True)
     assert_close("lse", lse[0, 0], lse_ref, TOL_LSE)
+
+
+def test_largest_grid_one_row_heads():
+    heads = 2**23 - 1                     # one 128-row tile per head: the most workgroups accepted
+    d = 64
+    announce(f"largest grid: B=1 H={heads} N=1 d={d} bf16 forward + backward")
+    dev = torch.device("cuda", 0)
+    inp = device_inputs(1, heads, 1, d, "bf16", seed=8392, device=dev, names=("q", "k", "v", "do"))
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.forward(q, k, v, causal=True, scale=scale)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, v), "one key per row: O must equal V"
+    assert torch.equal(dv, do), "one key per row: dV must equal dO"
+    assert float(dq.abs().max()) <= 1e-3 and float(dk.abs().max()) <= 1e-3
+    # lse at sampled heads against the oracle (one row each)
+    hs = torch.as_tensor(np.random.default_rng(0).choice(heads, 512, replace=False), device=dev)
+    q64, k64, v64 = (to64(t[0].index_select(0, hs)) for t in (q, k, v))
+    lse_s = lse[0].index_select(0, hs).cpu()
+    ref_lse = np.array([ref.forward_head(q64[i], k64[i], v64[i], True, scale)[1] for i in range(len(hs))])
+    assert_close("lse", lse_s, ref_lse, TOL_LSE)
+    # the FP8 forward's grid at the same size: O = V again (P = 1 is exact in E4M3)
+    del dq, dk, dv, do, o
+    q8, k8, v8 = (t.to(torch.float8_e4m3fn) for t in (q, k, v))
+    del q, k, v, inp
+    o8, lse8 = fa.forward_fp8(q8, k8, v8, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o8, v8.to(torch.bfloat16)), "FP8, one key per row: O must equal V"
+    assert bool(torch.isfinite(lse8).all())
