@@ -24,6 +24,9 @@ seed (workloads.device_inputs).
   then holds 2^32 - 512 work items).  With one key per row P = 1 exactly, so
   O = V and dV = dO bit for bit, lse = scale * q . k, and dS = 0 up to the
   rounding of D, so dQ and dK vanish.
+* The largest decoding merge grid: B*H*Nq = 2^26 - 32 rows of 64 threads (2^32
+  - 2048 work items), 32 queries over 64 zero keys in two chunks: every weight
+  is 1/64, so O is the mean of V and lse = ln 64.
 
 Named to run last: together these take about two minutes.
 """
@@ -162,3 +165,22 @@ def test_largest_grid_one_row_heads():
     torch.cuda.synchronize()
     assert torch.equal(o8, v8.to(torch.bfloat16)), "FP8, one key per row: O must equal V"
     assert bool(torch.isfinite(lse8).all())
+
+
+def test_largest_decode_merge_grid():
+    heads, nq, nk, d = 2**21 - 1, 32, 64, 64
+    announce(f"largest decode merge grid: B=1 H={heads} Nq={nq} Nk={nk} d={d} bf16, 2 chunks")
+    dev = torch.device("cuda", 0)
+    q = device_inputs(1, heads, nq, d, "bf16", seed=8393, device=dev, names=("q",))["q"]
+    v = device_inputs(1, heads, nk, d, "bf16", seed=8394, device=dev, names=("v",))["v"]
+    k = torch.zeros_like(v)
+    assert fa.fa_decode_num_splits(1, heads, nk, 2) == 2
+    o, lse = fa.decode(q, k, v, causal=False, scale=1.0 / math.sqrt(d), num_splits=2)
+    torch.cuda.synchronize()
+    assert float((lse.double() - math.log(nk)).abs().max()) <= TOL_LSE
+    err = 0.0
+    for h0 in range(0, heads, 1 << 16):                       # fp64 in slices of heads
+        sl = slice(h0, min(heads, h0 + (1 << 16)))
+        want = v[0, sl].double().mean(dim=1, keepdim=True)  # [h, 1, d], broadcast over the queries
+        err = max(err, float((o[0, sl].double() - want).abs().max()))
+    assert err <= TOL["bf16"], f"O: max|err| {err:.3g}"
