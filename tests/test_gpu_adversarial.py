@@ -1,0 +1,144 @@
+"""Adversarial score patterns against the fp64 oracle (needs an MI355X).
+
+The online softmax ("FlashAttention in NeurIPS 2022" section 2.1; "Как
+работает FlashAttention математически" sections 3-4) has to survive scores
+whose running maximum moves a lot:
+
+* rising scores, s_j = +j: every 64-key tile raises the row maximum by 64,
+  far past the lazy-rescale margin, so the output accumulator is rescaled on
+  every tile, and the weights of the early keys underflow to zero;
+* falling scores, s_j = -j: the first tile holds the maximum and no later tile
+  raises it.
+
+The magnitudes reach 999, where exp without the shift would overflow fp32.
+The inputs make every score an exact integer in both dtypes:
+  q = (1, 1, 0, ...),  k_j = ±(64 floor(j / 64), j mod 64, 0, ...)
+(every entry is exact in bf16), so the GPU and the oracle see the same scores.
+V and dO are N(0, 1).  Scale 1; N = 1000 (16 key tiles, the last ragged).
+
+O, lse, dV and decoding are held to the usual bars (1e-5 fp32 / 2e-2 bf16,
+lse 1e-3).  dQ and dK are not, and cannot be, at these magnitudes: dQ_r =
+scale sum_j P_rj (dP_rj - D_r) k_j cancels terms of size |k_j| ~ 1000 down to
+results of order ten, so any rounding of P, dP or D is multiplied by |k|.
+D_r = dO_r . O_r is formed from the stored O, which carries the output's
+rounding (fp32: 2^-24, bf16: 2^-9 relative per element), so its error scales
+with A_r = sum_c |dO_rc O_rc| rather than with |D_r|.  The bar adds, per
+element, a multiple of the size of the summed terms,
+  M_dQ[r, c] = scale sum_j P_rj (|dP_rj| + A_r) |k_jc|   (likewise M_dK over r, with |q_rc|),
+namely 1e-6 M (fp32: about 17 unit roundoffs) or 2^-7 M (bf16: four times the
+unit roundoff of O and of dS, both rounded to bf16), on top of the usual bar.
+With bf16 the rounding of O alone moves dQ by up to ~34 here (D off by 0.035,
+times sum_j P_rj k_j ~ 1000), more than the values themselves, so there the bar
+only catches non-finite or grossly wrong gradients; ordinary magnitudes are
+covered by the other backward tests.
+"""
+import numpy as np
+import pytest
+import torch
+
+import io_aware_tiled_attention_amd as fa
+from oracle import attention_ref as ref
+
+from gpu_helpers import TOL, TOL_LSE, announce, assert_close, bf16_ulp, grad_tol, require_gpu, to64
+
+pytestmark = pytest.mark.gpu
+
+N, D = 1000, 64
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def adversarial_inputs(dtype: str, seed: int):
+    """Head 0: rising scores s_j = j; head 1: falling scores s_j = -j."""
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    j = torch.arange(N, dtype=torch.float32)
+    q = torch.zeros(1, 2, N, D)
+    q[..., 0] = 1.0
+    q[..., 1] = 1.0
+    k = torch.zeros(1, 2, N, D)
+    for h, sign in ((0, 1.0), (1, -1.0)):
+        k[0, h, :, 0] = sign * 64.0 * torch.floor(j / 64.0)
+        k[0, h, :, 1] = sign * torch.remainder(j, 64.0)
+    g = torch.Generator().manual_seed(seed)
+    v = torch.randn(1, 2, N, D, generator=g)
+    do = torch.randn(1, 2, N, D, generator=g)
+    out = {n: t.to(td) for n, t in (("q", q), ("k", k), ("v", v), ("do", do))}
+    s = (out["q"].double() * out["k"].double()).sum(-1)
+    assert torch.equal(s[0, 0], j.double()) and torch.equal(s[0, 1], -j.double()), "scores must be exact"
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_and_falling_scores_forward_and_backward(dtype, causal):
+    announce(f"adversarial scores {dtype} N={N} d={D} causal={causal}")
+    inp = adversarial_inputs(dtype, seed=5150 + causal)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, causal=causal, scale=1.0)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal=causal, scale=1.0)
+    torch.cuda.synchronize()
+    o, lse, dq, dk, dv = (t.cpu() for t in (o, lse, dq, dk, dv))
+    q64, k64, v64, do64 = (to64(inp[n]) for n in ("q", "k", "v", "do"))
+    bf = dtype == "bf16"
+    for h in (0, 1):
+        o_r, lse_r = ref.forward_head(q64[0, h], k64[0, h], v64[0, h], causal, 1.0)
+        assert np.all(np.isfinite(lse_r))
+        assert_close(f"O[{h}]", o[0, h], o_r, TOL[dtype], bf16_output=bf)
+        assert_close(f"lse[{h}]", lse[0, h], lse_r, TOL_LSE)
+        dq_r, dk_r, dv_r = ref.backward_head(q64[0, h], k64[0, h], v64[0, h], do64[0, h], causal, 1.0)
+        assert_close(f"dV[{h}]", dv[0, h], dv_r, grad_tol(dtype, dv_r), bf16_output=bf)
+        m_dq, m_dk = term_sizes(q64[0, h], k64[0, h], v64[0, h], do64[0, h], o_r, lse_r, causal)
+        c = 1e-6 if dtype == "f32" else 2.0 ** -7
+        assert_within(f"dQ[{h}]", dq[0, h], dq_r, grad_tol(dtype, dq_r) + c * m_dq, bf)
+        assert_within(f"dK[{h}]", dk[0, h], dk_r, grad_tol(dtype, dk_r) + c * m_dk, bf)
+
+
+def term_sizes(q, k, v, do, o, lse, causal):
+    """Sizes of the terms that dQ and dK sum (fp64, from the oracle's O and lse):
+    M_dQ = sum_j P_rj (|dP_rj| + A_r) |k_j|, M_dK = sum_r P_rj (|dP_rj| + A_r) |q_r|,
+    with A_r = sum_c |dO_rc O_rc| the size of the terms of D_r."""
+    s = q @ k.T
+    if causal:
+        s = np.where(np.tril(np.ones_like(s, dtype=bool)), s, -np.inf)
+    p = np.exp(s - lse[:, None])
+    w = p * (np.abs(do @ v.T) + np.sum(np.abs(do * o), axis=1)[:, None])
+    return w @ np.abs(k), w.T @ np.abs(q)
+
+
+def assert_within(name, got, want, bar, bf16_output):
+    """|got - want| <= bar element by element (bar an array); bf16 outputs also
+    get one ulp of the reference."""
+    g = to64(got)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values in GPU output"
+    if bf16_output:
+        bar = np.maximum(bar, bf16_ulp(want))
+    err = np.abs(g - want)
+    worst = int(np.argmax(err / bar))
+    ratio = float(err.flat[worst] / bar.flat[worst])
+    print(f"    {name}: max|err| = {float(err.max()):.3e}, worst err/bar = {ratio:.2f} "
+          f"(bar there {float(bar.flat[worst]):.3e}), max|ref| = {float(np.abs(want).max()):.3f}", flush=True)
+    assert ratio <= 1.0, f"{name}: error {float(err.flat[worst]):.3e} > bar {float(bar.flat[worst]):.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("splits", [0, 1, 7])
+def test_rising_and_falling_scores_decode(dtype, splits):
+    """Split-KV decoding of the last 4 rows: with rising scores the chunks'
+    partial maxima differ by up to ~1000, so the merge weights of all but the
+    last chunk underflow; with falling scores the first chunk dominates."""
+    announce(f"adversarial scores decode {dtype} Nq=4 Nk={N} splits={splits}")
+    inp = adversarial_inputs(dtype, seed=5160)
+    dev = torch.device("cuda", 0)
+    qn = inp["q"][:, :, N - 4:].contiguous()
+    o, lse = fa.decode(qn.to(dev), inp["k"].to(dev), inp["v"].to(dev), causal=True, scale=1.0, num_splits=splits)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    q64, k64, v64 = (to64(t) for t in (qn, inp["k"], inp["v"]))
+    for h in (0, 1):
+        o_r, lse_r = ref.decode_head(q64[0, h], k64[0, h], v64[0, h], causal=True, scale=1.0)
+        assert_close(f"O[{h}]", o[0, h], o_r, TOL[dtype], bf16_output=dtype == "bf16")
+        assert_close(f"lse[{h}]", lse[0, h], lse_r, TOL_LSE)
