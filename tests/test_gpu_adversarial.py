@@ -17,7 +17,7 @@ The inputs make every score an exact integer in both dtypes:
 V and dO are N(0, 1).  Scale 1; N = 1000 (16 key tiles, the last ragged).
 
 O, lse, dV and decoding are held to the usual bars (1e-5 fp32 / 2e-2 bf16,
-lse 1e-3).  dQ and dK are not, and cannot be, at these magnitudes: dQ_r =
+lse 1e-3).  dQ and dK cannot be, at these magnitudes: dQ_r =
 scale sum_j P_rj (dP_rj - D_r) k_j cancels terms of size |k_j| ~ 1000 down to
 results of order ten, so any rounding of P, dP or D is multiplied by |k|.
 D_r = dO_r . O_r is formed from the stored O, which carries the output's
@@ -25,12 +25,15 @@ rounding (fp32: 2^-24, bf16: 2^-9 relative per element), so its error scales
 with A_r = sum_c |dO_rc O_rc| rather than with |D_r|.  The bar adds, per
 element, a multiple of the size of the summed terms,
   M_dQ[r, c] = scale sum_j P_rj (|dP_rj| + A_r) |k_jc|   (likewise M_dK over r, with |q_rc|),
-namely 1e-6 M (fp32: about 17 unit roundoffs) or 2^-7 M (bf16: four times the
-unit roundoff of O and of dS, both rounded to bf16), on top of the usual bar.
-With bf16 the rounding of O alone moves dQ by up to ~34 here (D off by 0.035,
-times sum_j P_rj k_j ~ 1000), more than the values themselves, so there the bar
-only catches non-finite or grossly wrong gradients; ordinary magnitudes are
-covered by the other backward tests.
+namely 1e-6 M in fp32 (about 17 unit roundoffs), on top of the usual bar:
+that is a parity check of fp32 dQ and dK.
+
+bf16 dQ and dK get NO parity check here.  The rounding of the stored bf16 O
+alone moves dQ by up to ~34 in this test (D off by 0.035, times
+sum_j P_rj k_j ~ 1000), more than the values themselves, so no bar derived
+from the rounding would say anything.  For bf16 the test only asserts that
+dQ and dK are finite (the online softmax did not overflow); parity of bf16
+gradients at ordinary magnitudes is what the other backward tests check.
 """
 import numpy as np
 import pytest
@@ -39,7 +42,7 @@ import torch
 import io_aware_tiled_attention_amd as fa
 from oracle import attention_ref as ref
 
-from gpu_helpers import TOL, TOL_LSE, announce, assert_close, bf16_ulp, grad_tol, require_gpu, to64
+from gpu_helpers import TOL, TOL_LSE, announce, assert_close, grad_tol, require_gpu, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -91,10 +94,16 @@ def test_rising_and_falling_scores_forward_and_backward(dtype, causal):
         assert_close(f"lse[{h}]", lse[0, h], lse_r, TOL_LSE)
         dq_r, dk_r, dv_r = ref.backward_head(q64[0, h], k64[0, h], v64[0, h], do64[0, h], causal, 1.0)
         assert_close(f"dV[{h}]", dv[0, h], dv_r, grad_tol(dtype, dv_r), bf16_output=bf)
+        if bf:
+            # finiteness only, not parity (see the module docstring)
+            for name, got in (("dQ", dq), ("dK", dk)):
+                assert bool(torch.isfinite(got[0, h]).all()), f"{name}[{h}]: non-finite bf16 gradient"
+                print(f"    {name}[{h}] (bf16): finite; no parity bar at these magnitudes", flush=True)
+            continue
         m_dq, m_dk = term_sizes(q64[0, h], k64[0, h], v64[0, h], do64[0, h], o_r, lse_r, causal)
-        c = 1e-6 if dtype == "f32" else 2.0 ** -7
-        assert_within(f"dQ[{h}]", dq[0, h], dq_r, grad_tol(dtype, dq_r) + c * m_dq, bf)
-        assert_within(f"dK[{h}]", dk[0, h], dk_r, grad_tol(dtype, dk_r) + c * m_dk, bf)
+        c = 1e-6
+        assert_within(f"dQ[{h}]", dq[0, h], dq_r, grad_tol(dtype, dq_r) + c * m_dq)
+        assert_within(f"dK[{h}]", dk[0, h], dk_r, grad_tol(dtype, dk_r) + c * m_dk)
 
 
 def term_sizes(q, k, v, do, o, lse, causal):
@@ -109,13 +118,10 @@ def term_sizes(q, k, v, do, o, lse, causal):
     return w @ np.abs(k), w.T @ np.abs(q)
 
 
-def assert_within(name, got, want, bar, bf16_output):
-    """|got - want| <= bar element by element (bar an array); bf16 outputs also
-    get one ulp of the reference."""
+def assert_within(name, got, want, bar):
+    """|got - want| <= bar element by element (bar an array; fp32 outputs)."""
     g = to64(got)
     assert np.all(np.isfinite(g)), f"{name}: non-finite values in GPU output"
-    if bf16_output:
-        bar = np.maximum(bar, bf16_ulp(want))
     err = np.abs(g - want)
     worst = int(np.argmax(err / bar))
     ratio = float(err.flat[worst] / bar.flat[worst])

@@ -19,26 +19,12 @@ def _gpu():
     require_gpu()
 
 
-def test_causal_bwd_4k_d64_heads():
-    """The backward problem: O and lse come from fa_forward on the same inputs."""
+def test_causal_bwd_4k_d64_all_heads():
+    """C5: all 4 x 16 heads compared whole; O and lse come from fa_forward on
+    the same inputs."""
     p = PROBLEMS["causal_bwd_4k_d64"]
-    announce(p.name)
-    inputs = make_inputs(p)
-    check_backward_heads(inputs, p.causal, p.scale, heads=[(0, 0), (1, 7), (2, 11), (3, 15)])
-
-
-def test_causal_bwd_4k_d64_all_heads_sampled_rows():
-    """Every fifth head of every batch, whole heads."""
-    p = PROBLEMS["causal_bwd_4k_d64"]
-    announce(p.name + " all heads")
-    inputs = make_inputs(p)
-    _, _, dq, dk, dv = gpu_backward(inputs, p.causal, p.scale)
-    q, k, v, do = (to64(inputs[n]) for n in ("q", "k", "v", "do"))
-    for b in range(p.B):
-        for h in range(0, p.H, 5):
-            dq_r, dk_r, dv_r = ref.backward_head(q[b, h], k[b, h], v[b, h], do[b, h], causal=True, scale=p.scale)
-            for name, got, want in (("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r)):
-                assert_close(f"{name}[{b},{h}]", got[b, h], want, TOL["bf16"], bf16_output=True)
+    announce(p.name + " (all 64 heads whole)")
+    check_backward_heads(make_inputs(p), p.causal, p.scale)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -63,19 +49,31 @@ def test_multi_block(dtype, d):
     check_backward_heads(inputs, True, 0.3 if dtype == "f32" else 1.0 / math.sqrt(d))
 
 
-def test_causal_4k_d128_backward_one_head():
+def test_causal_4k_d128_backward_eight_heads():
+    """The 4K d=128 backward shape: heads 0-7 of batch 0 (one per XCD) and
+    the last head, whole."""
     p = PROBLEMS["causal_4k_d128_bwd"]
-    announce(p.name)
+    announce(p.name + " (heads (0,0)-(0,7) and (3,31) whole)")
     inputs = make_inputs(p)
-    check_backward_heads(inputs, True, p.scale, heads=[(0, 0), (3, 31)])
+    check_backward_heads(inputs, True, p.scale, heads=[(0, h) for h in range(8)] + [(3, 31)])
 
 
 @pytest.mark.slow
-def test_causal_16k_d128_backward_one_head():
+def test_causal_16k_d128_backward_eight_heads():
+    """The 16K d=128 backward (the bench workload, not one of the five parity
+    configurations): heads 0-7 whole, one per XCD.  Its stressed keys (1% of
+    K scaled by 8) put probabilities near 1 on thousands of queries, so dV_j
+    sums thousands of sizeable terms P_ij dO_i, each with P_ij rounded to bf16
+    (the matrix cores' operand type).  A CPU emulation of that rounding alone
+    (fp64 otherwise) puts one element of head 4 at 0.0219 from the fp64 value
+    (reference 6.39693, emulated 6.375, exactly the GPU's result), past the
+    strict 2e-2.  So the gradients here are held to the strict bar or, where
+    the bf16 rounding of the operands can exceed it, to that rounding's
+    first-order bound; the count of elements above the strict bar is printed."""
     p = PROBLEMS["causal_16k_d128_bwd"]
-    announce(p.name)
+    announce(p.name + " (heads 0-7 whole)")
     inputs = make_inputs(p)
-    check_backward_heads(inputs, True, p.scale, heads=[(0, 17)])
+    check_backward_heads(inputs, True, p.scale, heads=[(0, h) for h in range(8)], operand_bound=True)
 
 
 def test_backward_matches_finite_differences_of_gpu_forward_sign():
