@@ -70,7 +70,8 @@ enum fa_status {
   FA_ERR_HIP = 7,       /* the HIP runtime reported an error at launch */
   FA_ERR_ALIGN = 8,     /* a tensor pointer is not 16-byte aligned */
   FA_ERR_MASK = 9,      /* block-sparse mask geometry invalid (see fa_forward_block_sparse) */
-  FA_ERR_DROPOUT = 10   /* dropout probability outside [0, 255/256] after rounding (see fa_forward_dropout) */
+  FA_ERR_DROPOUT = 10,  /* dropout probability outside [0, 255/256] after rounding (see fa_forward_dropout) */
+  FA_ERR_SCRATCH = 11   /* fa_backward_noalloc: the problem needs more than FA_NOALLOC_SCRATCH_BYTES of workspace */
 };
 
 /*
@@ -248,6 +249,26 @@ int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* do
 int fa_backward_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
                    int B, int H, int N, int d, int causal, float scale, int dtype,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_backward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc.  Same arguments (minus the workspace),
+ * validation, kernels and results as fa_backward, bit for bit.  The workspace
+ * lives in a device array of FA_NOALLOC_SCRATCH_BYTES inside the library,
+ * which each GPU the library runs on holds until the process ends; the call
+ * itself allocates and frees nothing.  Problems whose
+ * fa_backward_workspace_size exceeds FA_NOALLOC_SCRATCH_BYTES (B*H*N above
+ * about two million rows) return FA_ERR_SCRATCH.  All calls on one GPU share
+ * that GPU's array: calls that overlap in time on one GPU (on different
+ * streams or host threads) race and must be serialised by the caller.  The
+ * first call on each device looks the array up (hipGetSymbolAddress); make it
+ * outside a graph capture.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        int B, int H, int N, int d, int causal, float scale, int dtype, void* stream);
 
 /* Static English description of an fa_status value (never NULL). */
 const char* fa_strerror(int status);

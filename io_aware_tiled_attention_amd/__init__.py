@@ -18,7 +18,7 @@ from typing import Optional, Tuple
 
 from . import _lib
 from ._lib import (FA_BF16, FA_F32, FaError, fa_backward, fa_backward_block_sparse, fa_backward_dkdv,
-                   fa_backward_dq, fa_backward_dropout,
+                   fa_backward_dq, fa_backward_dropout, fa_backward_noalloc,
                    fa_backward_preprocess, fa_backward_workspace_size, fa_decode, fa_decode_num_splits,
                    fa_decode_workspace_size, fa_forward, fa_forward_block_sparse, fa_forward_dropout,
                    fa_forward_fp8, fa_strerror)
@@ -29,7 +29,7 @@ __all__ = ["forward", "forward_block_sparse", "forward_fp8", "backward", "backwa
            "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_forward_dropout",
            "fa_backward_dropout", "fa_forward_fp8", "fa_decode",
            "fa_decode_workspace_size", "fa_decode_num_splits", "fa_strerror", "load_library",
-           "backward_stages"]
+           "backward_stages", "backward_noalloc", "fa_backward_noalloc"]
 
 
 def load_library():
@@ -312,4 +312,31 @@ def backward_stages(q, k, v, o, do, lse, causal: bool = False, scale: Optional[f
                           dv.data_ptr(), B, H, N, d, causal, scale, dt, ws, wn, s)
     if st != 0:
         raise FaError(st, "fa_backward_dkdv")
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
+                     dq=None, dk=None, dv=None):
+    """The same result as :func:`backward` through fa_backward_noalloc, whose
+    workspace is the library's own per-GPU device array (no allocation by the
+    library; problems past FA_NOALLOC_SCRATCH_BYTES of workspace raise
+    FA_ERR_SCRATCH).  Calls that overlap in time on one GPU share that array
+    and race."""
+    import torch
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(name, t, q.shape, q.dtype, q.device)
+    _check("lse", lse, (B, H, N), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, q.shape, q.dtype, q.device)
+    st = fa_backward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                             causal, scale, _dtype_code(q), _stream_ptr(q.device))
+    if st != 0:
+        raise FaError(st, "fa_backward_noalloc")
     return dq, dk, dv

@@ -19,12 +19,15 @@ FA_BF16 = 1
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_DTYPE",
     5: "FA_ERR_SCALE", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP", 8: "FA_ERR_ALIGN", 9: "FA_ERR_MASK", 10: "FA_ERR_DROPOUT",
+    11: "FA_ERR_SCRATCH",
 }
+# FA_NOALLOC_SCRATCH_BYTES (include/fa.h): the workspace fa_backward_noalloc holds per GPU
+NOALLOC_SCRATCH_BYTES = 16 << 20
 EXPORTED = ("fa_forward", "fa_forward_block_sparse", "fa_backward", "fa_backward_block_sparse",
             "fa_backward_workspace_size",
             "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_forward_dropout",
             "fa_backward_dropout", "fa_forward_fp8", "fa_decode",
-            "fa_decode_workspace_size", "fa_decode_num_splits", "fa_strerror")
+            "fa_decode_workspace_size", "fa_decode_num_splits", "fa_backward_noalloc", "fa_strerror")
 
 _lock = threading.Lock()
 _lib = None
@@ -81,6 +84,8 @@ def load() -> ctypes.CDLL:
         lib.fa_decode_workspace_size.restype = sz
         lib.fa_decode_num_splits.argtypes = [i, i, i, i]
         lib.fa_decode_num_splits.restype = i
+        lib.fa_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        lib.fa_backward_noalloc.restype = i
         lib.fa_strerror.argtypes = [i]
         lib.fa_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -159,6 +164,11 @@ def fa_decode_workspace_size(B, H, Nq, Nk, d, num_splits) -> int:
 
 def fa_decode_num_splits(B, H, Nk, num_splits) -> int:
     return load().fa_decode_num_splits(B, H, Nk, num_splits)
+
+
+def fa_backward_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype, stream) -> int:
+    return load().fa_backward_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, int(causal), float(scale),
+                                      dtype, stream)
 
 
 def fa_strerror(status: int) -> str:

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa_gfx950.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_fwd_fp8.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_fwd_fp8.hip", "fa_noalloc.hip", "fa_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -330,6 +330,9 @@ const char* fa_strerror(int status) {
       return "invalid block mask geometry: mask_heads must be 1 or H, block_q a positive multiple of 32, "
              "block_k a positive multiple of 64, and N at most 65536";
     case FA_ERR_DROPOUT: return "invalid dropout probability: round(256 p) must lie in [0, 255]";
+    case FA_ERR_SCRATCH:
+      return "fa_backward_noalloc: the problem needs more workspace than the library's built-in "
+             "FA_NOALLOC_SCRATCH_BYTES; use fa_backward with a caller-owned workspace";
     default: return "unknown fa_status";
   }
 }

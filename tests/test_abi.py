@@ -101,6 +101,45 @@ def test_backward_workspace_exact_size_is_accepted_by_validation():
     assert bwd(ws_bytes=need, dq=0) == 1
 
 
+def bwd_noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, H=2,
+             N=64, d=64, causal=1, scale=0.125, dtype=_lib.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_backward_noalloc(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                  a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), 1), (dict(do=0), 1), (dict(lse=0), 1), (dict(dq=0), 1), (dict(dk=0), 1), (dict(dv=0), 1),
+    (dict(o=0), 1),
+    (dict(N=-5), 2), (dict(d=80), 3), (dict(dtype=7), 4), (dict(scale=float("-inf")), 5),
+    (dict(dv=FAKE + 6), 8),
+    # past the built-in scratch: more than 2^21 rows (16 MiB of workspace)
+    (dict(B=1, H=1, N=(1 << 21) + 1), 11), (dict(B=2, H=32, N=65536, d=128), 11),
+    # an invalid argument is reported before the scratch limit
+    (dict(B=2, H=32, N=65536, q=0), 1),
+])
+def test_backward_noalloc_rejects_invalid_arguments_before_any_hip_call(kw, status):
+    """fa_backward_noalloc validates exactly as fa_backward (no workspace
+    argument), then checks its built-in scratch size, all before touching
+    the device."""
+    assert bwd_noalloc(**kw) == status
+
+
+def test_backward_noalloc_empty_problem_is_ok():
+    assert bwd_noalloc(N=0) == 0
+    assert bwd_noalloc(B=0, q=0) == 0
+
+
+def test_backward_noalloc_scratch_limit_matches_the_workspace_size():
+    """2^21 rows fit exactly: the workspace is two 4-byte statistics per row."""
+    assert _lib.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert fa.workspace_size(1, 1, 1 << 21, 64) == _lib.NOALLOC_SCRATCH_BYTES
+    assert fa.workspace_size(1, 1, (1 << 21) + 1, 64) > _lib.NOALLOC_SCRATCH_BYTES
+    text = open(HEADER).read()
+    assert "#define FA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in text
+
+
 def test_workspace_size_is_linear_in_n_and_aligned():
     for d in (64, 128):
         for n in (1, 17, 4096, 16384):
