@@ -148,11 +148,14 @@ def time_steps(step, torch, steps, warmup):
 
 
 def kernel_table(p, avg):
-    """Per-kernel time and throughput.  FLOPs per launch follow the stated
-    convention split by products: the backward's 2.5x-forward budget is five
-    N x N x d products; dK/dV performs four of them (S, dP, dV, dK) and dQ
-    three (S, dP, dQ) -- S and dP are recomputed in both, so the two kernels
-    together execute 7/5 of the convention's backward FLOPs."""
+    """Per-kernel time and throughput.  The convention counts the backward as
+    2.5x the forward: five N x N x d products (S, dP, dV, dK, dQ; halved when
+    causal).  dK/dV executes four of them (S, dP, dV, dK), all method work.
+    dQ executes three (S, dP, dQ), but only dQ is method work: its S and dP
+    recompute what dK/dV already formed, the price of a backward without
+    atomics.  So each backward kernel reports its executed FLOPs and its
+    share of the method's FLOPs, with a fraction of peak on each basis; the
+    two kernels together execute 7/5 of the convention's backward FLOPs."""
     fwd_f, bwd_f = p.fwd_flops(), p.bwd_flops()
     unit = bwd_f / 5.0                       # one N x N x d product (halved when causal)
     elt = 2 if p.dtype == "bf16" else 4
@@ -160,20 +163,74 @@ def kernel_table(p, avg):
     tens = rows * p.d * elt
     out = {}
 
-    def mm(name, kernel, flops):
-        out[name] = {"kernel": kernel, "ms": avg[name], "flops": flops, "tflops": flops / avg[name] * 1e-9,
-                     "frac_peak": flops / avg[name] * 1e-9 / PEAK_BF16_TFLOPS}
+    def mm(name, kernel, executed, method):
+        ms = avg[name]
+        out[name] = {"kernel": kernel, "ms": ms, "flops": method, "executed_flops": executed,
+                     "method_flops": method,
+                     "tflops": method / ms * 1e-9, "frac_peak": method / ms * 1e-9 / PEAK_BF16_TFLOPS,
+                     "executed_tflops": executed / ms * 1e-9,
+                     "frac_peak_executed": executed / ms * 1e-9 / PEAK_BF16_TFLOPS}
 
     sfx = "_bf16" if p.dtype == "bf16" else ""     # bf16 has its own backward kernels
-    mm("fwd", "fa_fwd_kernel", fwd_f)
-    mm("bwd_dkdv", f"fa_bwd_dkdv{sfx}_kernel", 4 * unit)
-    mm("bwd_dq", f"fa_bwd_dq{sfx}_kernel", 3 * unit)
+    mm("fwd", "fa_fwd_kernel", fwd_f, fwd_f)
+    mm("bwd_dkdv", f"fa_bwd_dkdv{sfx}_kernel", 4 * unit, 4 * unit)
+    mm("bwd_dq", f"fa_bwd_dq{sfx}_kernel", 3 * unit, 1 * unit)
     pre_bytes = 2 * tens + 3 * rows * 4                        # read O, dO, lse; write D, -lse
     out["bwd_pre"] = {"kernel": "fa_bwd_pre_kernel", "ms": avg["bwd_pre"], "bytes": pre_bytes,
                       "gbs": pre_bytes / avg["bwd_pre"] * 1e-6}
     out["bwd_total"] = {"ms": avg["bwd_pre"] + avg["bwd_dkdv"] + avg["bwd_dq"]}
     out["bwd_total"]["tflops"] = bwd_f / out["bwd_total"]["ms"] * 1e-9
     out["bwd_total"]["frac_peak"] = out["bwd_total"]["tflops"] / PEAK_BF16_TFLOPS
+    out["bwd_total"]["executed_tflops"] = 7 * unit / out["bwd_total"]["ms"] * 1e-9
+    return out
+
+
+PROBE_LIB = os.path.join(ROOT, "io_aware_tiled_attention_amd", "libfa_probe_gfx950.so")
+
+
+def mfma_peak_measurement(torch, dev, iters=20000):
+    """The attainable matrix-core rate of this GPU: v_mfma_f32_32x32x16_bf16
+    with every operand in registers (libfa_probe_gfx950.so, include/fa_probe.h),
+    on N(0,1) bf16 operands, at one and two waves per SIMD; the larger rate
+    is the measured peak.  Under sustained matrix-core load the clock sits
+    below the 2.4 GHz of the published 2.5 PFLOP/s."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is missing: build with `python -m io_aware_tiled_attention_amd.build`")
+    lib = ctypes.CDLL(PROBE_LIB)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.fa_probe_mfma_bf16.argtypes = [vp, vp, i, i, vp]
+    lib.fa_probe_mfma_bf16.restype = i
+    lib.fa_probe_mfma_bf16_flops.argtypes = [i, i]
+    lib.fa_probe_mfma_bf16_flops.restype = ctypes.c_double
+    g = torch.Generator().manual_seed(11)
+    ops = torch.randn(8 * 64 * 8, generator=g).to(torch.bfloat16).to(dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {"what": "register-only v_mfma_f32_32x32x16_bf16, N(0,1) bf16 operands, 16 products per iteration "
+                   f"cycling 4 A x 4 B fragments, {iters} iterations per wave"}
+    best = 0.0
+    for w in (1, 2):
+        wgs = 256 * w
+        sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+
+        def run():
+            st = lib.fa_probe_mfma_bf16(ops.data_ptr(), sink.data_ptr(), wgs, iters, stream)
+            assert st == 0, st
+        for _ in range(2):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        tf = lib.fa_probe_mfma_bf16_flops(wgs, iters) / ms * 1e-9
+        out[f"tflops_{w}_wave_per_simd"] = tf
+        best = max(best, tf)
+    out["tflops"] = best
+    out["frac_of_published_peak"] = best / PEAK_BF16_TFLOPS
     return out
 
 
@@ -665,6 +722,9 @@ def main(argv=None):
     roofline = {"bound": "mfma", "kernel": kt[dom]["kernel"], "achieved": kt[dom]["tflops"],
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": kt[dom]["tflops"] / PEAK_BF16_TFLOPS,
                 "traffic": traffic, "flops_per_launch": kt[dom]["flops"], "avg_launch_ms": kt[dom]["ms"]}
+    mp = mfma_peak_measurement(torch, dev)
+    roofline["measured_peak"] = mp["tflops"]
+    roofline["frac_of_measured_peak"] = kt[dom]["tflops"] / mp["tflops"]
 
     extra = {}
     if not args.no_extra:
@@ -705,9 +765,11 @@ def main(argv=None):
         "config": {"workload": f"{p.name}: causal attention forward + backward", "B": p.B, "H": p.H,
                    "N": p.N, "d": p.d, "causal": p.causal, "flops_per_step": total_flops,
                    "accumulation": "fp32"},
-        "fwd": {"tflops": kt["fwd"]["tflops"], "frac_peak": kt["fwd"]["frac_peak"], "ms": kt["fwd"]["ms"]},
+        "fwd": {"tflops": kt["fwd"]["tflops"], "frac_peak": kt["fwd"]["frac_peak"], "ms": kt["fwd"]["ms"],
+                "frac_of_measured_peak": kt["fwd"]["tflops"] / mp["tflops"]},
         "bwd": {"tflops": kt["bwd_total"]["tflops"], "frac_peak": kt["bwd_total"]["frac_peak"],
-                "ms": kt["bwd_total"]["ms"]},
+                "ms": kt["bwd_total"]["ms"], "frac_of_measured_peak": kt["bwd_total"]["tflops"] / mp["tflops"]},
+        "mfma_peak": mp,
         "kernels": kt,
         "roofline": roofline,
         "extra": extra,

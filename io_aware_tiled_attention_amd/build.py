@@ -20,6 +20,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa_gfx950.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# measurement library (not the attention path): the register-only MFMA rate
+PROBE_NAME = "libfa_probe_gfx950.so"
+PROBE_PATH = os.path.join(PKG, PROBE_NAME)
+PROBE_SOURCES = ["mfma_peak.hip"]
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_fwd_fp8.hip", "fa_noalloc.hip", "fa_api.cpp"]
 ARCH = "gfx950"
 
@@ -64,14 +68,19 @@ def build(jobs: int = 4, save_temps: str | None = None, verbose: bool = False) -
         return obj
 
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+    link(cc, objs[:len(SOURCES)], LIB_PATH)
+    link(cc, objs[len(SOURCES):], PROBE_PATH)
+    return LIB_PATH
+
+
+def link(cc: str, objs, path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, path)
 
 
 def main(argv=None):

@@ -17,7 +17,10 @@ The inputs make every score an exact integer in both dtypes:
 V and dO are N(0, 1).  Scale 1; N = 1000 (16 key tiles, the last ragged).
 
 O, lse, dV and decoding are held to the usual bars (1e-5 fp32 / 2e-2 bf16,
-lse 1e-3).  dQ and dK cannot be, at these magnitudes: dQ_r =
+lse 1e-3), except bf16 dV: with every query's weight on the last keys, dV_j
+sums up to N sizeable terms P_ij dO_i whose P_ij are rounded to bf16 (the
+matrix cores' operand type), which can move it past 2e-2; there it is held
+to the strict bar or to the first-order bound of that rounding.  dQ and dK cannot be, at these magnitudes: dQ_r =
 scale sum_j P_rj (dP_rj - D_r) k_j cancels terms of size |k_j| ~ 1000 down to
 results of order ten, so any rounding of P, dP or D is multiplied by |k|.
 D_r = dO_r . O_r is formed from the stored O, which carries the output's
@@ -42,7 +45,8 @@ import torch
 import io_aware_tiled_attention_amd as fa
 from oracle import attention_ref as ref
 
-from gpu_helpers import TOL, TOL_LSE, announce, assert_close, grad_tol, require_gpu, to64
+from gpu_helpers import (TOL, TOL_LSE, announce, assert_close, assert_close_or_operand_bound, grad_tol,
+                         operand_rounding_terms, require_gpu, to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,7 +97,13 @@ def test_rising_and_falling_scores_forward_and_backward(dtype, causal):
         assert_close(f"O[{h}]", o[0, h], o_r, TOL[dtype], bf16_output=bf)
         assert_close(f"lse[{h}]", lse[0, h], lse_r, TOL_LSE)
         dq_r, dk_r, dv_r = ref.backward_head(q64[0, h], k64[0, h], v64[0, h], do64[0, h], causal, 1.0)
-        assert_close(f"dV[{h}]", dv[0, h], dv_r, grad_tol(dtype, dv_r), bf16_output=bf)
+        if bf:
+            # dV_j sums up to N terms P_ij dO_i with P_ij near 1, each P rounded
+            # to bf16 before the product: strict bar, or that rounding's bound
+            _, _, m_dv = operand_rounding_terms(q64[0, h], k64[0, h], v64[0, h], do64[0, h], causal, 1.0)
+            assert_close_or_operand_bound(f"dV[{h}]", dv[0, h], dv_r, m_dv)
+        else:
+            assert_close(f"dV[{h}]", dv[0, h], dv_r, grad_tol(dtype, dv_r))
         if bf:
             # finiteness only, not parity (see the module docstring)
             for name, got in (("dQ", dq), ("dK", dk)):
