@@ -13,17 +13,18 @@
 //     un-normalised output O^T (d x 32, fp32) in registers for the whole
 //     sweep over keys;
 //   * K and V stream through LDS in tiles of BC = 64 keys, global -> LDS
-//     directly (buffer_load ... lds), two stages deep: while tile j is being
-//     consumed, K and V of tile j+1 are in flight;
+//     directly (buffer_load ... lds), two stages deep at d = 128 and three at
+//     d = 64 (bf16): while tile j is being consumed, K and V of the next one
+//     or two tiles are in flight, and each wave waits with a counted vmcnt
+//     for its own copies of tile j+1 only;
 //   * per tile each wave computes S^T = K_j Q_i^T on the matrix cores, so
 //     that each lane holds 32 scores of ONE query: the row max needs only an
 //     in-lane reduction and one exchange with the partner lane l^32
 //     (v_permlane32_swap), and the rescale of O by exp(m_old - m_new) is one
 //     per-lane scalar;
-//   * a wave's matrix and vector work do not overlap each other (measured),
-//     so S of a tile is computed right before its softmax; overlap comes from
-//     the other wave on the SIMD.  (Issuing S of the next tile before the
-//     softmax only cost 32 registers and ~2%.)
+//   * S of a tile is computed right before its softmax: issuing S of the
+//     next tile first cost 32 registers and measured ~2% slower, the other
+//     wave on the SIMD providing the overlap of matrix and vector work;
 //   * the online-softmax update ("FlashAttention in NeurIPS 2022" section 2.1;
 //     "Как работает FlashAttention математически" sections 3-4) keeps O
 //     un-normalised and divides by l once at the end; the shift inside the
@@ -52,14 +53,31 @@ constexpr int kFwdThreads = kFwdWaves * 64;
 // Block-sparse: the key tiles a workgroup visits are listed in LDS (TileList,
 // N <= 64 * kListMax = 65536), with one bit per wave.
 
+// K/V stages: NST - 1 tiles are in flight while one is consumed.  bf16 at
+// d = 64 takes three: a tile then carries half the matrix work of d = 128,
+// too little to cover the latency of the next tile's copy with one tile of
+// prefetch, and three 16 KiB stages still leave room for three workgroups
+// per CU.  d = 128 keeps two (64 KiB, two workgroups per CU).
+template <typename T, int D>
+constexpr int fwd_stages() { return (sizeof(T) == 2 && D == 64) ? 3 : 2; }
+
 template <typename T, int D>
 struct FwdSmem {
+  static constexpr int NST = fwd_stages<T, D>();
   static constexpr int TILE = kFwdBC * D * (int)sizeof(T);   // bytes of one K or V tile
-  // [K stage 0][K stage 1][V stage 0][V stage 1]
-  static constexpr int BYTES = 4 * TILE;
+  // [K stages][V stages]
+  static constexpr int BYTES = 2 * NST * TILE;
+  // copy instructions each wave issues per K+V tile (1 KiB each)
+  static constexpr int PER = 2 * (TILE / 1024) / kFwdWaves;
+  static_assert((NST - 2) * PER <= 63, "vmcnt is 6 bits");
   __device__ static lds_u8* k(lds_u8* base, int st) { return base + st * TILE; }
-  __device__ static lds_u8* v(lds_u8* base, int st) { return base + (2 + st) * TILE; }
+  __device__ static lds_u8* v(lds_u8* base, int st) { return base + (NST + st) * TILE; }
 };
+
+template <int N>
+__device__ __forceinline__ void fwd_wait_vmem_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // SPARSE: block-sparse attention ("Overview of Flash Attention series",
 // Block-sparse Flashattention).  mask[mh][qb][kb] != 0 keeps the block of
@@ -108,8 +126,10 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   const size_t head = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * G::R;
   const rsrc_t rq = make_rsrc(Q + head, head_bytes);
-  const rsrc_t rk = make_rsrc(K + head, head_bytes);
-  const rsrc_t rv = make_rsrc(V + head, head_bytes);
+  // K/V tiles are copied with tile_to_lds_async; each wave waits for its
+  // own copies (counted vmcnt) before the barrier that publishes a tile
+  const u32x4 rk = rsrc_words(K + head, head_bytes);
+  const u32x4 rv = rsrc_words(V + head, head_bytes);
 
   const int qw0 = q0 + w * kFwdQW;
   const int myq = qw0 + r32;
@@ -181,26 +201,47 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     else return i <= wave_last;
   };
 
-  // Prologue: K and V of the first visited tile (and K of the second)
-  // resident; its S computed.
+  constexpr int NST = L::NST;
+  auto load = [&](int i, int st) {
+    tile_to_lds_async<T, D, kFwdBC, kFwdWaves>(rk, L::k(smem, st), tile_of(i) * kFwdBC, w, lane);
+    tile_to_lds_async<T, D, kFwdBC, kFwdWaves>(rv, L::v(smem, st), tile_of(i) * kFwdBC, w, lane);
+  };
+  // Tile `it` has landed once at most the copies of the tiles issued after
+  // it, up to NST - 2 of them, are outstanding (copies complete in issue
+  // order).
+  auto wait_tile = [&](int it) {
+    if constexpr (NST > 2) {
+      if (it + NST - 2 < n_act) {
+        fwd_wait_vmem_n<(NST - 2) * L::PER>();
+        return;
+      }
+    }
+    wait_vmem();
+  };
+
+  // Prologue: the first NST - 1 visited tiles in flight, the first landed.
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i)
+    if (i < n_act) load(i, i);
+  // Take the compiler's wait for the Q loads here, once: at their first use
+  // inside the loop it would also drain the K/V copies in flight.
+#pragma unroll
+  for (int c = 0; c < D / KC; ++c) asm volatile("" : "+v"(qf[c]));
   f32x16 s_cur[NKB];
   if (n_act > 0) {
-    tile_to_lds<T, D, kFwdBC, kFwdWaves>(rk, L::k(smem, 0), tile_of(0) * kFwdBC, w, lane);
-    tile_to_lds<T, D, kFwdBC, kFwdWaves>(rv, L::v(smem, 0), tile_of(0) * kFwdBC, w, lane);
-    wait_vmem();
+    wait_tile(0);
     __syncthreads();
   }
 
+  int st = 0;                 // stage of tile it
+  int st_next = NST - 1;      // stage of tile it + NST - 1 (read in iteration it - 1)
   for (int it = 0; it < n_act; ++it) {
     const int j = tile_of(it);
     const int kv0 = j * kFwdBC;
-    if (it + 1 < n_act) {
-      tile_to_lds<T, D, kFwdBC, kFwdWaves>(rk, L::k(smem, (it + 1) & 1), tile_of(it + 1) * kFwdBC, w, lane);
-      tile_to_lds<T, D, kFwdBC, kFwdWaves>(rv, L::v(smem, (it + 1) & 1), tile_of(it + 1) * kFwdBC, w, lane);
-    }
+    if (it + NST - 1 < n_act) load(it + NST - 1, st_next);
 
     if (active(it)) {
-      compute_st(s_cur, L::k(smem, it & 1));
+      compute_st(s_cur, L::k(smem, st));
       const bool masked = (CAUSAL && kv0 + kFwdBC - 1 > qw0) || (kv0 + kFwdBC > N);
       if (masked) {
         // keys allowed for this lane: key <= min(N-1, myq) (causal) or key <= N-1
@@ -254,7 +295,7 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
       }
 
       // O^T += V^T P^T, with P^T straight from the registers of S^T.
-      const lds_u8* vs = L::v(smem, it & 1);
+      const lds_u8* vs = L::v(smem, st);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -274,8 +315,10 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
         }
     }
 
-    wait_vmem();
+    if (it + 1 < n_act) wait_tile(it + 1);
     __syncthreads();
+    st = st + 1 == NST ? 0 : st + 1;
+    st_next = st_next + 1 == NST ? 0 : st_next + 1;
   }
 
   // Epilogue: O = O_acc / l (deferred normalisation), lse = shift + ln l;
@@ -310,8 +353,8 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int BH = a.B * a.H;
   const int n_qtiles = (a.N + kFwdBR - 1) / kFwdBR;
   const dim3 grid(n_qtiles * BH), block(kFwdThreads);
-  // resident workgroups per XCD: 32 CUs x (2 for bf16, 1 for fp32)
-  const int group = wg_group(n_qtiles, 32 * (sizeof(T) == 2 ? 2 : 1));
+  // resident workgroups per XCD: 32 CUs x (bf16: 2 at d = 128, 3 at d = 64; fp32: 1)
+  const int group = wg_group(n_qtiles, 32 * (sizeof(T) == 2 ? (D == 64 ? 3 : 2) : 1));
   hipLaunchKernelGGL(kern, grid, block, bytes, stream, static_cast<const T*>(a.q),
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<T*>(a.o),
                      a.lse, a.N, BH, n_qtiles, group, a.scale, a.mask, a.H, a.mask_heads, a.block_q, a.block_k, a.drop);
