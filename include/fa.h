@@ -65,7 +65,8 @@ enum fa_status {
                            B * H * ceil(N / 128) is 2^23 or more (a launch's work items must fit in 32 bits) */
   FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 */
   FA_ERR_DTYPE = 4,     /* dtype is not an fa_dtype */
-  FA_ERR_SCALE = 5,     /* scale is NaN, infinite or negative (FP8 descale factors: not finite or <= 0) */
+  FA_ERR_SCALE = 5,     /* scale is NaN, infinite or negative, or scale * log2(e) overflows float (FP8: a descale
+                           factor not finite or <= 0, or scale * q_descale * k_descale * log2(e) overflows float) */
   FA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than fa_backward_workspace_size */
   FA_ERR_HIP = 7,       /* the HIP runtime reported an error at launch */
   FA_ERR_ALIGN = 8,     /* a tensor pointer is not 16-byte aligned */

@@ -40,7 +40,6 @@ def common_flags():
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # no packed fp32 VALU forms anywhere in device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-munsafe-fp-atomics",
         "-I", INCLUDE, "-I", CSRC,
         "-Wall", "-Wno-unused-function",
     ]

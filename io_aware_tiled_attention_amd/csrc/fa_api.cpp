@@ -18,12 +18,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int64_t kMaxTileThreads = 512;
 constexpr int64_t kDecodeThreads = 64;
 
+// The bf16 kernels fold the score factor into base-2 exponentials:
+// factor * log2(e) must be a finite float, or every probability would be NaN.
+bool exp2_factor_finite(double factor) { return std::isfinite((float)(factor * 1.4426950408889634)); }
+
 // Shape check shared by every entry point; `empty` is set for B*H*N == 0.
 int check_shape(int B, int H, int N, int d, int dtype, float scale, bool* empty) {
   if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+  if (!std::isfinite(scale) || scale < 0.f || !exp2_factor_finite(scale)) return FA_ERR_SCALE;
   // Sizes must fit the kernels' index arithmetic: rows and per-head byte
   // offsets use 32-bit ints, whole-tensor offsets 64-bit.  A ragged last
   // tile addresses up to kRowSlack rows past N (reads there are dropped by
@@ -160,6 +164,8 @@ int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* 
   const float ds[] = {q_descale, k_descale, v_descale};
   for (float x : ds)
     if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_SCALE;
+  // the kernel's score factor scale * q_descale * k_descale * log2(e)
+  if (!exp2_factor_finite((double)scale * q_descale * k_descale)) return FA_ERR_SCALE;
   if (empty) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;

@@ -191,11 +191,6 @@ __device__ __forceinline__ void tile_to_lds_async(u32x4 src, lds_u8* tile, int r
   }
 }
 
-// fp32 atomic add at byte offset `voff` of a buffer (dropped past its end).
-__device__ __forceinline__ void atomic_add_f32(rsrc_t r, int voff, float v) {
-  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, voff, 0, 0);
-}
-
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Transposed bf16 A fragment (M = columns, K = rows) from a swizzled tile:

@@ -73,6 +73,8 @@ def bwd(**kw):
     (dict(d=32), 3), (dict(d=96), 3), (dict(d=0), 3), (dict(d=256), 3),
     (dict(dtype=2), 4), (dict(dtype=-1), 4),
     (dict(scale=float("nan")), 5), (dict(scale=float("inf")), 5), (dict(scale=-0.5), 5),
+    # finite, but scale * log2(e) overflows float (the kernels' exponent factor)
+    (dict(scale=3e38), 5), (dict(scale=3e38, dtype=_lib.FA_F32), 5),
     (dict(q=FAKE + 2), 8), (dict(lse=FAKE + 4), 8), (dict(o=FAKE + 8), 8),
 ])
 def test_forward_rejects_invalid_arguments(kw, status):
@@ -408,9 +410,19 @@ def fwd_fp8(**kw):
     (dict(q=0), 1), (dict(o=0), 1), (dict(N=-1), 2), (dict(N=1 << 23, q=0), 2), (dict(d=96), 3),
     (dict(scale=float("nan")), 5), (dict(qs=0.0), 5), (dict(ks=-1.0), 5), (dict(vs=float("inf")), 5),
     (dict(v=FAKE + 8), 8), (dict(N=1 << 22, q=0), 1),
+    # finite descale factors whose product with scale and log2(e) overflows float
+    (dict(scale=1.0, qs=1e30, ks=1e30), 5), (dict(scale=3e38, qs=1.0, ks=1.0), 5),
+    (dict(scale=1e30, qs=1e5, ks=1e4), 5),
 ])
 def test_forward_fp8_rejects_invalid_arguments(kw, status):
     assert fwd_fp8(**kw) == status
+
+
+def test_scale_just_below_the_exponent_factor_overflow_passes_validation():
+    """2e38 * log2(e) is still a finite float: validation passes it and then
+    stops at the next check (a NULL tensor)."""
+    assert fwd(scale=2e38, o=0) == 1
+    assert fwd_fp8(scale=1e30, qs=1e5, ks=1e2, o=0) == 1
 
 
 def test_forward_fp8_empty_problem_is_a_noop():
