@@ -26,8 +26,7 @@ Sources (page title -> part used):
   invariants after each K/V block).
 * "Как работает FlashAttention математически" (How FlashAttention works
   mathematically), sections 3-4 (online softmax; the running output kept
-  un-normalised and divided once at the end) and section 6 (the per-Q-block
-  loop).
+  un-normalised and divided once at the end).
 * "Overview of Flash Attention series", section *Backward Pass of
   flashattention*: dV = P^T dO, dP = dO V^T, D_i = P_i:^T dP_i: = do_i^T o_i,
   dS = P o (dP - D), dq_i = sum_j dS_ij k_j, dk_j = sum_i dS_ij q_i.
@@ -297,36 +296,68 @@ def online_softmax_blocks(s_row, v, block: int):
     return history
 
 
+def _block_stats(s_blk, v_blk):
+    """One key block's own softmax statistics for each score row:
+    m_b = rowmax(S_b), f_b = exp(S_b - m_b), l_b = rowsum(f_b), and the
+    block's un-normalised output f_b V_b.  A row whose scores in the block
+    are all -inf (masked) has m_b = -inf, l_b = 0 and output 0."""
+    m_b = np.max(s_blk, axis=1)
+    safe = np.where(np.isfinite(m_b), m_b, 0.0)
+    f_b = np.exp(s_blk - safe[:, None])          # exp(-inf) = 0 for masked entries
+    return m_b, np.sum(f_b, axis=1), f_b @ v_blk
+
+
+def _fold(m1, l1, o1, m2, l2, o2, normalised: bool):
+    """Combine the statistics of two disjoint key blocks, row by row, by the
+    decomposition of the softmax over a concatenated vector x = [x1, x2]
+    ("Overview of Flash Attention series", Tiling; the same update of m and l
+    in section 2.1 of "FlashAttention in NeurIPS 2022"):
+      m = max(m1, m2),  l = e^(m1 - m) l1 + e^(m2 - m) l2,
+    and for the output either the un-normalised sum
+      O~ = e^(m1 - m) O~1 + e^(m2 - m) O~2
+    or, with each O_k normalised by its own l_k,
+      O = (e^(m1 - m) l1 O1 + e^(m2 - m) l2 O2) / l.
+    A side whose m is -inf (no unmasked score yet) carries weight 0."""
+    m = np.maximum(m1, m2)
+    safe = np.where(np.isfinite(m), m, 0.0)
+    w1 = np.where(np.isfinite(m1), np.exp(m1 - safe), 0.0)
+    w2 = np.where(np.isfinite(m2), np.exp(m2 - safe), 0.0)
+    l = w1 * l1 + w2 * l2
+    if not normalised:
+        return m, l, w1[:, None] * o1 + w2[:, None] * o2
+    with np.errstate(invalid="ignore", divide="ignore"):
+        inv = np.where(l > 0, 1.0 / l, 0.0)
+    return m, l, (inv * w1 * l1)[:, None] * o1 + (inv * w2 * l2)[:, None] * o2
+
+
 def blockwise_forward_head(q, k, v, block_q: int, block_k: int, causal: bool = False,
                            scale: Optional[float] = None, form: str = "deferred",
                            check_invariants: bool = False):
-    """Tiled forward for one head in the pages' loop order: returns (O, lse).
+    """Tiled forward for one head: returns (O, lse).
 
     Q is cut into blocks of ``block_q`` rows and K, V into blocks of
-    ``block_k`` rows (primer: T_r = ceil(N/B_r), T_c = ceil(N/B_c)).  For
-    each Q block (the primer's "V2" order: Q outer, K/V inner; the result
-    does not depend on the order) the running m, l, O start at -inf, 0, 0
-    and each K/V block updates them by the online-softmax rule:
-      m_new = max(m, rowmax(S_ij))
-      l_new = exp(m - m_new) l + rowsum(exp(S_ij - m_new))
-    and the output either
+    ``block_k`` rows (primer: T_r = ceil(N/B_r), T_c = ceil(N/B_c)); the
+    query blocks are independent (the primer's "V2" order, Q outer; the
+    result does not depend on the order).  For a query block the statistics
+    (m, l, O) start as those of no keys at all (-inf, 0, 0), and each key
+    block in turn is folded in: its own statistics (:func:`_block_stats`)
+    are combined with the running ones by the two-block decomposition of
+    the softmax (:func:`_fold`).  The output is kept either
 
-    * ``form="normalised"``: O = (l/l_new) exp(m - m_new) O
-      + (1/l_new) exp(S_ij - m_new) V_j   (section 6 of the aivaro page,
-      the coreui o-update), or
-    * ``form="deferred"``: O = exp(m - m_new) O + exp(S_ij - m_new) V_j and a
-      single division by l after the last block (section 4 of the aivaro
-      page: kept un-normalised, normalised once at the end).
+    * ``form="normalised"``: O normalised after every block (the running
+      output of section 2.1 of "FlashAttention in NeurIPS 2022"), or
+    * ``form="deferred"``: un-normalised, divided by l once after the last
+      block ("Как работает FlashAttention математически", section 4).
 
-    With ``check_invariants`` the Theorem 1 invariants ("Overview of Flash
-    Attention series", Correctness) are asserted after each K/V block:
-    m = rowmax of the scores seen so far, l = rowsum(exp(S_seen - m)),
-    normalised O = softmax(S_seen) V_seen.  A row with no unmasked key yet
-    keeps m = -inf, l = 0, O = 0 (the -inf - (-inf) case is taken as weight 0).
+    lse = m + ln l at the end.  With ``check_invariants`` the invariants of
+    Theorem 1 ("Overview of Flash Attention series", Correctness) are
+    asserted after each key block: m = rowmax of the scores seen so far,
+    l = rowsum(exp(S_seen - m)), and the normalised O = softmax(S_seen) V_seen.
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     if form not in ("deferred", "normalised"):
         raise ValueError(form)
+    normalised = form == "normalised"
     n_q, d = q.shape
     n_k = k.shape[0]
     if scale is None:
@@ -336,28 +367,19 @@ def blockwise_forward_head(q, k, v, block_q: int, block_k: int, causal: bool = F
     s_full = scores(q, k, scale, causal) if check_invariants else None
     for qs in range(0, n_q, block_q):
         rows = np.arange(qs, min(qs + block_q, n_q))
-        q_i = q[rows]
         m = np.full(rows.size, -np.inf)
         l = np.zeros(rows.size)
         o = np.zeros((rows.size, v.shape[1]))
         for ks in range(0, n_k, block_k):
             cols = np.arange(ks, min(ks + block_k, n_k))
-            s_ij = scale * (q_i @ k[cols].T)
+            s_blk = scale * (q[rows] @ k[cols].T)
             if causal:
-                s_ij = np.where(cols[None, :] > rows[:, None], -np.inf, s_ij)
-            m_new = np.maximum(m, np.max(s_ij, axis=1))
-            # weight 0 for rows that have seen no unmasked key yet
-            safe = np.where(np.isfinite(m_new), m_new, 0.0)
-            alpha = np.where(np.isfinite(m), np.exp(m - safe), 0.0)
-            p_ij = np.exp(s_ij - safe[:, None])
-            l_new = alpha * l + np.sum(p_ij, axis=1)
-            if form == "normalised":
+                s_blk = np.where(cols[None, :] > rows[:, None], -np.inf, s_blk)
+            m_b, l_b, o_b = _block_stats(s_blk, v[cols])
+            if normalised:
                 with np.errstate(invalid="ignore", divide="ignore"):
-                    inv = np.where(l_new > 0, 1.0 / l_new, 0.0)
-                o = (l * inv * alpha)[:, None] * o + inv[:, None] * (p_ij @ v[cols])
-            else:
-                o = alpha[:, None] * o + p_ij @ v[cols]
-            m, l = m_new, l_new
+                    o_b = np.where(l_b[:, None] > 0, o_b / l_b[:, None], 0.0)
+            m, l, o = _fold(m, l, o, m_b, l_b, o_b, normalised)
             if check_invariants:
                 seen = s_full[rows][:, :cols[-1] + 1]
                 ref_m = np.max(seen, axis=1)
@@ -367,9 +389,9 @@ def blockwise_forward_head(q, k, v, block_q: int, block_k: int, causal: bool = F
                 ref_l = np.sum(np.exp(seen[fin] - ref_m[fin][:, None]), axis=1)
                 np.testing.assert_allclose(l[fin], ref_l, rtol=1e-12, atol=0)
                 ref_o = (np.exp(seen[fin] - ref_m[fin][:, None]) / ref_l[:, None]) @ v[:cols[-1] + 1]
-                got_o = o[fin] if form == "normalised" else o[fin] / l[fin][:, None]
+                got_o = o[fin] if normalised else o[fin] / l[fin][:, None]
                 np.testing.assert_allclose(got_o, ref_o, rtol=1e-12, atol=1e-12)
-        if form == "deferred":
+        if not normalised:
             o = o / l[:, None]
         o_all[rows] = o
         lse_all[rows] = m + np.log(l)
