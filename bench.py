@@ -480,7 +480,7 @@ def gemm_ceiling_measurement(torch, dev, steps, n=16384):
 CONFIG_NAMES = ["single_head_f32", "gpt2_small_bf16", "causal_4k_d128", "causal_16k_d128", "causal_bwd_4k_d64"]
 
 
-def config_measurement(fa, torch, dev, warm=10, timed=50):
+def config_measurement(fa, torch, dev, warm=10, timed=50, names=None):
     """Per-call timing of each of the five parity configurations: `warm`
     untimed calls, then `timed` calls each bracketed by its own pair of HIP
     events on the launch stream; median, p10 and p90 in ms and TFLOP/s at the
@@ -492,7 +492,7 @@ def config_measurement(fa, torch, dev, warm=10, timed=50):
     raw = fa.load_library()
     stream = torch.cuda.current_stream().cuda_stream
     out = {}
-    for name in CONFIG_NAMES:
+    for name in (names or CONFIG_NAMES):
         p = PROBLEMS[name]
         inputs = make_inputs(p)
         q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
@@ -654,6 +654,8 @@ def main(argv=None):
                     help="only the split-KV decoding measurement (one JSON line; for kernel traces)")
     ap.add_argument("--configs-only", action="store_true",
                     help="only the per-call timing of the five parity configurations (one JSON line)")
+    ap.add_argument("--config", action="append", choices=CONFIG_NAMES, default=None,
+                    help="with --configs-only: only this configuration (repeatable)")
     ap.add_argument("--sparse-only", action="store_true",
                     help="only the block-sparse forward and backward measurement (one JSON line)")
     ap.add_argument("--fp8-only", action="store_true",
@@ -662,6 +664,8 @@ def main(argv=None):
                     help="only the dropout measurement (one JSON line; for kernel traces)")
     ap.add_argument("--decode-shape", type=int, default=None,
                     help="with --decode-only: only this entry of the decoding shapes")
+    ap.add_argument("--mfma-peak-only", action="store_true",
+                    help="only the register-only MFMA rate (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM counters)")
     args = ap.parse_args(argv)
@@ -692,8 +696,11 @@ def main(argv=None):
         print(json.dumps({"copy_calibration": {"bytes_read_per_copy": 4 * n, "bytes_written_per_copy": 4 * n,
                                                "copies": 3}}), flush=True)
         return 0
+    if args.mfma_peak_only:
+        print(json.dumps({"mfma_peak": mfma_peak_measurement(torch, dev)}), flush=True)
+        return 0
     if args.configs_only:
-        print(json.dumps({"configs": config_measurement(fa, torch, dev)}), flush=True)
+        print(json.dumps({"configs": config_measurement(fa, torch, dev, names=args.config)}), flush=True)
         return 0
     if args.sparse_only:
         print(json.dumps({"block_sparse_16k_d128": sparse_measurement(fa, torch, dev, max(3, args.steps))}), flush=True)

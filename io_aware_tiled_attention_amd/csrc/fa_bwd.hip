@@ -668,6 +668,12 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
 }
 
 // ---------------------------------------------------------------- 3. dQ
+// K/V stages of the bf16 dQ kernel: three at d = 64 (each 64-key tile then
+// carries half the matrix work of d = 128, too little to cover the next
+// tile's copy with one tile of prefetch; 48 KiB still fits three workgroups
+// per CU), two at d = 128 (64 KiB, two workgroups per CU).
+template <int D>
+constexpr int dq_stages() { return D == 64 ? 3 : 2; }
 constexpr int kDqWaves = 4;
 constexpr int kDqQW = 32;                       // query rows per wave
 constexpr int kDqBR = kDqWaves * kDqQW;         // query rows per workgroup
@@ -878,8 +884,13 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   constexpr int NKB = kDqBC / 32;
   constexpr int NDB = D / 32, NC = D / KC;
   constexpr int TILE = kDqBC * G::R;
-  // [K st0][K st1][V st0][V st1] (block-sparse: then the tile list)
-  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[4 * TILE + (SPARSE ? kListBytes : 0)];
+  // K/V stages: NST - 1 tiles in flight while one is consumed (three at
+  // d = 64, whose tiles carry half the matrix work of d = 128)
+  constexpr int NST = dq_stages<D>();
+  constexpr int PER = 2 * (TILE / 1024) / kDqWaves;   // copy instructions per wave per K+V tile
+  static_assert((NST - 2) * PER <= 63, "vmcnt is 6 bits");
+  // [K stages][V stages] (block-sparse: then the tile list)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[2 * NST * TILE + (SPARSE ? kListBytes : 0)];
   lds_u8* smem = (lds_u8*)smem_raw;
 
   const int tid = threadIdx.x;
@@ -917,8 +928,8 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   }
   const rsrc_t rnl = make_rsrc(nlse + (size_t)bh * N, (uint32_t)N * 4u);
   const rsrc_t rdd = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
-  const float nl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rnl, myq * 4, 0, 0));
-  const float dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdd, myq * 4, 0, 0));
+  float nl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rnl, myq * 4, 0, 0));
+  float dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdd, myq * 4, 0, 0));
   if constexpr (!DROP) (void)dpar;
 
   // Loop-invariant per-lane LDS offsets (the swizzle depends on the row
@@ -945,7 +956,7 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   // 64-key tile in one mask column since block_k is a multiple of 64).  A
   // wave that reaches a tile has every one of its rows past the tile's first
   // key, so no row it computes has lse = -inf.
-  const TileList tl = tile_list_at(smem + 4 * TILE);
+  const TileList tl = tile_list_at(smem + 2 * NST * TILE);
   int n_act = ntiles;
   if constexpr (SPARSE) {
     const int tk_n = (N + sp.block_k - 1) / sp.block_k;
@@ -977,25 +988,46 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
 
   auto load_tile = [&](int j, int st) {
     tile_to_lds_async<bf16, D, kDqBC, kDqWaves>(rk, smem + st * TILE, j * kDqBC, w, lane);
-    tile_to_lds_async<bf16, D, kDqBC, kDqWaves>(rv, smem + (2 + st) * TILE, j * kDqBC, w, lane);
+    tile_to_lds_async<bf16, D, kDqBC, kDqWaves>(rv, smem + (NST + st) * TILE, j * kDqBC, w, lane);
+  };
+  // Tile `it` has landed once at most the copies of the tiles issued after
+  // it, up to NST - 2 of them, are outstanding (copies complete in issue
+  // order).
+  auto wait_tile = [&](int it) {
+    if constexpr (NST > 2) {
+      if (it + NST - 2 < n_act) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * PER) : "memory");
+        return;
+      }
+    }
+    wait_vmem();
   };
 
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-  if (n_act > 0) load_tile(tile_of(0), 0);
-  wait_vmem();
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i)
+    if (i < n_act) load_tile(tile_of(i), i);
+  // Take the compiler's waits for the Q, dO and statistics loads here, once:
+  // at their first use inside the loop they would also drain the K/V copies
+  // in flight.
+#pragma unroll
+  for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(qf[c]), "+v"(dof[c]));
+  asm volatile("" : "+v"(nl), "+v"(dd));
+  if (n_act > 0) wait_tile(0);
   __syncthreads();
 
   // Visited tile number `it` (tile_of(it)) from staging buffer ST.
-  auto tile = [&](int it, auto st_c, auto masked_c) {
+  auto tile = [&](int it, auto st_c, auto masked_c) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
     constexpr bool MASKED = decltype(masked_c)::value;
-    constexpr int KB = ST * TILE, VB = (2 + ST) * TILE;
+    constexpr int KB = ST * TILE, VB = (NST + ST) * TILE;
     const int j = tile_of(it);
     const int kv0 = j * kDqBC;
-    if (it + 1 < n_act) load_tile(tile_of(it + 1), ST ^ 1);
+    // the stage of tile it + NST - 1 held tile it - 1, read in the last iteration
+    if (it + NST - 1 < n_act) load_tile(tile_of(it + NST - 1), (ST + NST - 1) % NST);
     if (!MASKED || active(it)) {
       bool msk = false;
       int last = 0;
@@ -1076,12 +1108,13 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) dq_mma(kb, ds[kb]);
     }
-    wait_vmem();
+    if (it + 1 < n_act) wait_tile(it + 1);
     __syncthreads();
   };
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
   using Msk = std::integral_constant<bool, true>;
   using NoMsk = std::integral_constant<bool, false>;
   // Leading tiles that no wave needs to mask: keys below the workgroup's
@@ -1091,17 +1124,39 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   // branch taken only where needed).
   const int n_plain = SPARSE ? 0 : (CAUSAL ? min(ntiles, q0 / kDqBC) : N / kDqBC);
   int j = 0;
-  for (; j + 1 < n_plain; j += 2) {
-    tile(j, S0{}, NoMsk{});
-    tile(j + 1, S1{}, NoMsk{});
-  }
-  if (j < n_plain) {
-    tile(j, S0{}, NoMsk{});
-    ++j;
-  }
-  for (; j < n_act; ++j) {
-    if (j & 1) tile(j, S1{}, Msk{});
-    else tile(j, S0{}, Msk{});
+  if constexpr (NST == 2) {
+    for (; j + 1 < n_plain; j += 2) {
+      tile(j, S0{}, NoMsk{});
+      tile(j + 1, S1{}, NoMsk{});
+    }
+    if (j < n_plain) {
+      tile(j, S0{}, NoMsk{});
+      ++j;
+    }
+    for (; j < n_act; ++j) {
+      if (j & 1) tile(j, S1{}, Msk{});
+      else tile(j, S0{}, Msk{});
+    }
+  } else {
+    // The stage of visited tile j is j % NST; the plain run is unrolled over
+    // the stages so that every LDS address is a compile-time offset.
+    for (; j + NST - 1 < n_plain; j += NST) {
+      tile(j, S0{}, NoMsk{});
+      tile(j + 1, S1{}, NoMsk{});
+      tile(j + 2, S2{}, NoMsk{});
+    }
+    for (; j < n_act; ++j) {
+      const int st = j % NST;
+      if (j < n_plain) {
+        if (st == 0) tile(j, S0{}, NoMsk{});
+        else if (st == 1) tile(j, S1{}, NoMsk{});
+        else tile(j, S2{}, NoMsk{});
+      } else {
+        if (st == 0) tile(j, S0{}, Msk{});
+        else if (st == 1) tile(j, S1{}, Msk{});
+        else tile(j, S2{}, Msk{});
+      }
+    }
   }
 
   // dQ = scale * acc; lane holds query myq, d = db*32 + acc_row(i, g).
@@ -1159,7 +1214,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
                          stream, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                          static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.dsum, a.nlse,
                          static_cast<bf16*>(a.dq), a.N, BH, n_qtiles,
-                         wg_group(n_qtiles, 64), a.scale, sp, a.drop);   // 2 workgroups per CU
+                         wg_group(n_qtiles, 32 * (D == 64 ? 3 : 2)), a.scale, sp, a.drop);   // 3 / 2 workgroups per CU
     } else {
       constexpr int bytes = 4 * kDqBC * D * (int)sizeof(T) + (SPARSE ? kListBytes : 0);
       auto kern = fa_bwd_dq_kernel<T, D, CAUSAL, SPARSE, DROP>;
