@@ -231,6 +231,22 @@ def mfma_peak_measurement(torch, dev, iters=20000):
         best = max(best, tf)
     out["tflops"] = best
     out["frac_of_published_peak"] = best / PEAK_BF16_TFLOPS
+    # the same instruction stream on all-zero operands: the matrix cores'
+    # switching power, and with it the clock the power manager allows,
+    # depends on the operand bits; with zeros the chip runs at its top clock
+    zeros = torch.zeros_like(ops)
+    wgs = 256
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        assert lib.fa_probe_mfma_bf16(zeros.data_ptr(), sink.data_ptr(), wgs, iters, stream) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        assert lib.fa_probe_mfma_bf16(zeros.data_ptr(), sink.data_ptr(), wgs, iters, stream) == 0
+    e1.record()
+    torch.cuda.synchronize()
+    out["tflops_zero_operands_1_wave_per_simd"] = lib.fa_probe_mfma_bf16_flops(wgs, iters) / (e0.elapsed_time(e1) / 5) * 1e-9
     return out
 
 
