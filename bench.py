@@ -2,10 +2,13 @@
 """Throughput of the exact-attention hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-fa_forward (O, lse) then the backward's three stages (D = rowsum(dO o O),
-the key-parallel dK/dV kernel and the query-parallel dQ kernel), on the
-long-context causal problem B=1, H=32, N=16384, d=128, bf16 (fp32
-accumulation).  Inputs are resident in HBM before timing starts.
+fa_forward (O, lse) then fa_backward (dQ, dK, dV), on the long-context
+causal problem B=1, H=32, N=16384, d=128, bf16 (fp32 accumulation).
+Inputs are resident in HBM before timing starts.  For bf16, fa_backward
+runs the query-parallel dQ kernel with the row statistics D = rowsum(dO o O)
+and -lse folded in, then the key-parallel dK/dV kernel.  The per-kernel
+table times each kernel alone, through the staged entry points
+(preprocess, dK/dV, dQ), in a separate pass.
 
 FLOP counting convention: forward 4*B*H*N^2*d, halved when causal; backward
 2.5x forward.  The value is total (forward + backward) FLOPs per step over
@@ -117,10 +120,21 @@ class Step:
                                          int(self.p.causal), self.p.scale, self.dt, p.ws.data_ptr(), self.ws_bytes,
                                          self.stream), "fa_backward_dq")
 
+    def backward(self):
+        p = self
+        self._ck(self.lib.fa_backward(p.q.data_ptr(), p.k.data_ptr(), p.v.data_ptr(), p.o.data_ptr(), p.do.data_ptr(),
+                                      p.lse.data_ptr(), p.dq.data_ptr(), p.dk.data_ptr(), p.dv.data_ptr(), self.p.B,
+                                      self.p.H, self.p.N, self.p.d, int(self.p.causal), self.p.scale, self.dt,
+                                      p.ws.data_ptr(), self.ws_bytes, self.stream), "fa_backward")
+
+    # one step: the public calls, fa_forward then fa_backward (which, for bf16,
+    # runs dQ with the row statistics folded in, then dK/dV)
+    STEP = ("fwd", "bwd")
+    # the per-kernel breakdown: the staged entry points, one kernel each
     STAGES = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
 
     def run(self, events=None):
-        fns = (self.forward, self.bwd_pre, self.bwd_dkdv, self.bwd_dq)
+        fns = (self.forward, self.backward)
         if events is None:
             for fn in fns:
                 fn()
@@ -130,24 +144,45 @@ class Step:
             fn()
             events[i + 1].record()
 
+    def run_staged(self, events):
+        events[0].record()
+        for i, fn in enumerate((self.forward, self.bwd_pre, self.bwd_dkdv, self.bwd_dq)):
+            fn()
+            events[i + 1].record()
+
 
 def time_steps(step, torch, steps, warmup):
+    """Wall time per step (host clock around `steps` steps, bracketed by
+    synchronisations) and the mean forward and backward times (HIP events)."""
     for _ in range(warmup):
         step.run()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(Step.STEP) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         step.run(evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    per = {name: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, name in enumerate(Step.STEP)}
+    return (t1 - t0) * 1e3 / steps, {name: sum(v) / len(v) for name, v in per.items()}
+
+
+def time_kernels(step, torch, reps):
+    """Mean time of each kernel of the step, one HIP-event pair per kernel,
+    through the staged entry points (forward, preprocess, dK/dV, dQ)."""
+    for _ in range(2):
+        step.run_staged([torch.cuda.Event(enable_timing=True) for _ in range(5)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(reps)]
+    for i in range(reps):
+        step.run_staged(evs[i])
+    torch.cuda.synchronize()
     per = {name: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, name in enumerate(Step.STAGES)}
-    avg = {name: sum(v) / len(v) for name, v in per.items()}
-    return (t1 - t0) * 1e3 / steps, avg
+    return {name: sum(v) / len(v) for name, v in per.items()}
 
 
-def kernel_table(p, avg):
+def kernel_table(p, avg, step_avg):
     """Per-kernel time and throughput.  The convention counts the backward as
     2.5x the forward: five N x N x d products (S, dP, dV, dK, dQ; halved when
     causal).  dK/dV executes four of them (S, dP, dV, dK), all method work.
@@ -178,7 +213,9 @@ def kernel_table(p, avg):
     pre_bytes = 2 * tens + 3 * rows * 4                        # read O, dO, lse; write D, -lse
     out["bwd_pre"] = {"kernel": "fa_bwd_pre_kernel", "ms": avg["bwd_pre"], "bytes": pre_bytes,
                       "gbs": pre_bytes / avg["bwd_pre"] * 1e-6}
-    out["bwd_total"] = {"ms": avg["bwd_pre"] + avg["bwd_dkdv"] + avg["bwd_dq"]}
+    # the backward as fa_backward runs it (bf16: dQ with the row statistics
+    # folded in, then dK/dV), timed in the step; the staged sum for reference
+    out["bwd_total"] = {"ms": step_avg["bwd"], "staged_ms": avg["bwd_pre"] + avg["bwd_dkdv"] + avg["bwd_dq"]}
     out["bwd_total"]["tflops"] = bwd_f / out["bwd_total"]["ms"] * 1e-9
     out["bwd_total"]["frac_peak"] = out["bwd_total"]["tflops"] / PEAK_BF16_TFLOPS
     out["bwd_total"]["executed_tflops"] = 7 * unit / out["bwd_total"]["ms"] * 1e-9
@@ -735,8 +772,8 @@ def main(argv=None):
     p = PROBLEMS[args.workload]
     inputs = make_inputs(p, with_do=True)
     step = Step(fa, torch, inputs, p, dev)
-    ms_step, avg = time_steps(step, torch, args.steps, args.warmup)
-    kt = kernel_table(p, avg)
+    ms_step, step_avg = time_steps(step, torch, args.steps, args.warmup)
+    kt = kernel_table(p, time_kernels(step, torch, args.steps), step_avg)
 
     total_flops = p.fwd_flops() + p.bwd_flops()
     value = total_flops / ms_step * 1e-9
@@ -755,8 +792,8 @@ def main(argv=None):
         del step
         torch.cuda.empty_cache()
         s4 = Step(fa, torch, make_inputs(p4, with_do=True), p4, dev)
-        ms4, avg4 = time_steps(s4, torch, max(5, args.steps // 2), 3)
-        k4 = kernel_table(p4, avg4)
+        ms4, step4 = time_steps(s4, torch, max(5, args.steps // 2), 3)
+        k4 = kernel_table(p4, time_kernels(s4, torch, max(5, args.steps // 2)), step4)
         extra[p4.name] = {"B": p4.B, "H": p4.H, "N": p4.N, "d": p4.d, "causal": True, "ms_per_step": ms4,
                           "fwd_tflops": k4["fwd"]["tflops"], "fwd_frac_peak": k4["fwd"]["frac_peak"],
                           "bwd_tflops": k4["bwd_total"]["tflops"], "bwd_frac_peak": k4["bwd_total"]["frac_peak"]}
@@ -774,9 +811,9 @@ def main(argv=None):
         torch.cuda.empty_cache()
         ceil = gemm_ceiling_measurement(torch, dev, 5)
         g16 = ceil["bf16_tflops"]
-        ceil["frac_of_bf16_gemm"] = {"fwd": kt["fwd"]["tflops"] / g16, "bwd_dkdv": kt["bwd_dkdv"]["tflops"] / g16,
-                                     "bwd_dq": kt["bwd_dq"]["tflops"] / g16,
-                                     "bwd_total": kt["bwd_total"]["tflops"] / g16}
+        ceil["frac_of_bf16_gemm"] = {"fwd": kt["fwd"]["tflops"] / g16, "bwd_dkdv": kt["bwd_dkdv"]["executed_tflops"] / g16,
+                                     "bwd_dq": kt["bwd_dq"]["executed_tflops"] / g16,
+                                     "bwd_total_executed": kt["bwd_total"]["executed_tflops"] / g16}
         if "fp8_tflops" in ceil:
             ceil["fp8_fwd_frac_of_fp8_gemm"] = extra["fp8_16k_d128"]["tflops"] / ceil["fp8_tflops"]
         extra["gemm_ceiling"] = ceil
@@ -788,8 +825,9 @@ def main(argv=None):
         "config": {"workload": f"{p.name}: causal attention forward + backward", "B": p.B, "H": p.H,
                    "N": p.N, "d": p.d, "causal": p.causal, "flops_per_step": total_flops,
                    "accumulation": "fp32"},
-        "fwd": {"tflops": kt["fwd"]["tflops"], "frac_peak": kt["fwd"]["frac_peak"], "ms": kt["fwd"]["ms"],
-                "frac_of_measured_peak": kt["fwd"]["tflops"] / mp["tflops"]},
+        "fwd": {"tflops": p.fwd_flops() / step_avg["fwd"] * 1e-9,
+                "frac_peak": p.fwd_flops() / step_avg["fwd"] * 1e-9 / PEAK_BF16_TFLOPS, "ms": step_avg["fwd"],
+                "frac_of_measured_peak": p.fwd_flops() / step_avg["fwd"] * 1e-9 / mp["tflops"]},
         "bwd": {"tflops": kt["bwd_total"]["tflops"], "frac_peak": kt["bwd_total"]["frac_peak"],
                 "ms": kt["bwd_total"]["ms"], "frac_of_measured_peak": kt["bwd_total"]["tflops"] / mp["tflops"]},
         "mfma_peak": mp,

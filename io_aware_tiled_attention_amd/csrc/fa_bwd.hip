@@ -869,12 +869,19 @@ void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
 // The two 32-key halves of a tile are processed one after the other so that
 // the first half's dS is already packed to bf16 while the second half's
 // products run.
-template <int D, bool CAUSAL, bool SPARSE, bool DROP>
+//
+// PRE: this kernel also does the preprocess pass (it runs first then, before
+// dK/dV): each lane forms D_i = do_i . o_i and -lse_i for its own query from O
+// and lse, uses them, and writes them to the workspace for the dK/dV kernel.
+// The sum follows the preprocess kernel's order exactly (8-element chunks,
+// then the chunks 8, 4, 2 and 1 apart combined), so the gradients equal
+// those of the staged entry points bit for bit.
+template <int D, bool CAUSAL, bool SPARSE, bool DROP, bool PRE>
 __global__ __launch_bounds__(kDqThreads, 2)
 void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-                           const bf16* __restrict__ dO, const float* __restrict__ dsum,
-                           const float* __restrict__ nlse, bf16* __restrict__ dQ, int N, int BH, int n_qtiles,
-                           int group, float scale, SparseArgs sp, DropParams dpar) {
+                           const bf16* __restrict__ dO, const bf16* __restrict__ O, const float* __restrict__ LSE,
+                           float* __restrict__ dsum, float* __restrict__ nlse, bf16* __restrict__ dQ, int N, int BH,
+                           int n_qtiles, int group, float scale, SparseArgs sp, DropParams dpar) {
   using M = Mfma<bf16>;
   using G = Tile<bf16, D>;
   using X = ExpDomain<bf16>;
@@ -928,8 +935,37 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   }
   const rsrc_t rnl = make_rsrc(nlse + (size_t)bh * N, (uint32_t)N * 4u);
   const rsrc_t rdd = make_rsrc(dsum + (size_t)bh * N, (uint32_t)N * 4u);
-  float nl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rnl, myq * 4, 0, 0));
-  float dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdd, myq * 4, 0, 0));
+  float nl, dd;
+  if constexpr (PRE) {
+    // lane group g holds the 8-element chunks t = 2c + g of its query's row
+    const rsrc_t ro = make_rsrc(O + head, head_bytes);
+    const rsrc_t rls = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
+    float part[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const Frag of = M::load(ro, myq * G::R + (c * KC + g * KPL) * 2);
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += (float)of[e] * (float)dof[c][e];
+      part[c] = acc;
+    }
+    // chunks 8, 4 and 2 apart (c 4, 2 and 1 apart), then the partner lane's (1 apart)
+#pragma unroll
+    for (int h = NC / 2; h > 0; h >>= 1)
+#pragma unroll
+      for (int c = 0; c < h; ++c) part[c] = part[c] + part[c + h];
+    dd = pair_sum(part[0]);
+    nl = -X::from_lse(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rls, myq * 4, 0, 0)));
+    if (g == 0) {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dd), rdd, myq * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(nl), rnl, myq * 4, 0, 0);
+    }
+  } else {
+    (void)O;
+    (void)LSE;
+    nl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rnl, myq * 4, 0, 0));
+    dd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdd, myq * 4, 0, 0));
+  }
   if constexpr (!DROP) (void)dpar;
 
   // Loop-invariant per-lane LDS offsets (the swizzle depends on the row
@@ -1177,6 +1213,20 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   const int n_qtiles = (a.N + kDqBR - 1) / kDqBR;
   SparseArgs sp;
   if constexpr (SPARSE) sp = SparseArgs{a.mask, a.H, a.mask_heads, a.block_q, a.block_k};
+  // The whole bf16 backward runs dQ first, with the preprocess pass folded
+  // into it (PRE), then dK/dV, which reads the statistics dQ wrote.
+  if constexpr (sizeof(T) == 2) {
+    if (stages == (kStagePre | kStageDkDv | kStageDq)) {
+      hipLaunchKernelGGL((fa_bwd_dq_bf16_kernel<D, CAUSAL, SPARSE, DROP, true>), dim3(n_qtiles * BH),
+                         dim3(kDqThreads), 0, stream, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                         static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout),
+                         static_cast<const bf16*>(a.o), a.lse, a.dsum, a.nlse, static_cast<bf16*>(a.dq), a.N, BH,
+                         n_qtiles, wg_group(n_qtiles, 32 * (D == 64 ? 3 : 2)), a.scale, sp, a.drop);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      stages = kStageDkDv;
+    }
+  }
   if (stages & kStagePre) {
     constexpr int RPB = 256 / (D / (16 / (int)sizeof(T)));
     const size_t blocks = (rows + RPB - 1) / RPB;
@@ -1210,10 +1260,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   }
   if (stages & kStageDq) {
     if constexpr (sizeof(T) == 2) {
-      hipLaunchKernelGGL((fa_bwd_dq_bf16_kernel<D, CAUSAL, SPARSE, DROP>), dim3(n_qtiles * BH), dim3(kDqThreads), 0,
-                         stream, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
-                         static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.dsum, a.nlse,
-                         static_cast<bf16*>(a.dq), a.N, BH, n_qtiles,
+      hipLaunchKernelGGL((fa_bwd_dq_bf16_kernel<D, CAUSAL, SPARSE, DROP, false>), dim3(n_qtiles * BH),
+                         dim3(kDqThreads), 0, stream, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
+                         static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), nullptr, nullptr,
+                         a.dsum, a.nlse, static_cast<bf16*>(a.dq), a.N, BH, n_qtiles,
                          wg_group(n_qtiles, 32 * (D == 64 ? 3 : 2)), a.scale, sp, a.drop);   // 3 / 2 workgroups per CU
     } else {
       constexpr int bytes = 4 * kDqBC * D * (int)sizeof(T) + (SPARSE ? kListBytes : 0);
