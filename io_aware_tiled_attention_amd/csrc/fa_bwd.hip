@@ -341,10 +341,12 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
 // ---------------------------------------------------------------- 2b. dK, dV (bf16)
 // Eight waves over 128 keys: waves w and w + 4 own the same 32 keys (slice
 // w % 4) and take the first and the second 32-row query sub-block of every
-// 64-row block, so each SIMD runs two waves.  K and V stay resident in LDS;
-// each wave holds its K slice as B fragments in registers (read once) and
-// reads its V fragments per block -- holding both would not leave room for
-// two waves per SIMD.  Every LDS address is a
+// 64-row block, so each SIMD runs two waves of a workgroup.  K and V stay
+// resident in LDS; at d = 128 each wave holds its K slice as B fragments in
+// registers (read once) and reads its V fragments per block -- holding both
+// would not leave room for two waves per SIMD.  At d = 64 (no dropout) two
+// workgroups share a CU instead (kv_two_per_cu), and every operand is read
+// from LDS where it is used.  Every LDS address is a
 // per-lane offset computed once plus a compile-time constant: the block loop
 // is unrolled over the two staging buffers, and blocks that cross no diagonal
 // and no end of the sequence run a body without any masking.  At the end the
@@ -374,8 +376,17 @@ struct KvCfg {
   static_assert(STAGE + DO0 + 16 * G::R < 65536, "stage offsets fit the ds_read immediate");
 };
 
+// Two workgroups per CU at d = 64 (four waves per SIMD, at most 128
+// registers): the second workgroup covers the first's waits on its staged
+// blocks.  To fit, each wave reads its K fragments from LDS at every use
+// instead of holding them, and reads its other operands without a
+// one-step-ahead copy.  The dropout instantiations, which would spill at 128
+// registers, keep one workgroup per CU and the d = 128 layout.
+template <int D, bool DROP>
+constexpr bool kv_two_per_cu() { return D == 64 && !DROP; }
+
 template <int D, bool CAUSAL, bool SPARSE, bool DROP>
-__global__ __launch_bounds__(kKvThreads, 1)
+__global__ __launch_bounds__(kKvThreads, (kv_two_per_cu<D, DROP>() ? 4 : 1))
 void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                              const bf16* __restrict__ dO, const float* __restrict__ dsum,
                              const float* __restrict__ nlse, bf16* __restrict__ dK, bf16* __restrict__ dV, int N,
@@ -500,9 +511,12 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
   if (n_act > 0) load_block(q_begin + block_of(0) * BQ, 0);
   wait_vmem();
   __syncthreads();
-  Frag kf[NC];   // this wave's K slice as B fragments, read once
+  constexpr bool KREG = !kv_two_per_cu<D, DROP>();
+  Frag kf[KREG ? NC : 1];   // this wave's K slice as B fragments, read once
+  if constexpr (KREG) {
 #pragma unroll
-  for (int c = 0; c < NC; ++c) kf[c] = M::lds(smem + ka[c]);
+    for (int c = 0; c < NC; ++c) kf[c] = M::lds(smem + ka[c]);
+  }
 
   // Visited query block number `it` (64 rows from q_begin + block_of(it) * 64)
   // from staging buffer ST; MASKED also handles the causal diagonal and keys
@@ -527,21 +541,29 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
       if constexpr (DROP) rb = drop_bytes_queries(dpar.k0, dpar.k1, dpar.offset, (unsigned)bh, mykey, qsb, g, lane);
       // S = Q K^T and dP = dO V^T: rows = queries, column = this lane's key.
       f32x16 s = f32x16{}, dp = f32x16{};
-      Frag fq[2], fd[2], fv[2];
-      fq[0] = M::lds(sb + C::Q0 + qa[0]);
-      fd[0] = M::lds(sb + C::DO0 + qa[0]);
-      fv[0] = M::lds(smem + ka[0] + C::KTILE);
+      if constexpr (KREG) {
+        Frag fq[2], fd[2], fv[2];
+        fq[0] = M::lds(sb + C::Q0 + qa[0]);
+        fd[0] = M::lds(sb + C::DO0 + qa[0]);
+        fv[0] = M::lds(smem + ka[0] + C::KTILE);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int cur = c & 1;
-        if (c + 1 < NC) {
-          fq[cur ^ 1] = M::lds(sb + C::Q0 + qa[c + 1]);
-          fd[cur ^ 1] = M::lds(sb + C::DO0 + qa[c + 1]);
-          fv[cur ^ 1] = M::lds(smem + ka[c + 1] + C::KTILE);
+        for (int c = 0; c < NC; ++c) {
+          const int cur = c & 1;
+          if (c + 1 < NC) {
+            fq[cur ^ 1] = M::lds(sb + C::Q0 + qa[c + 1]);
+            fd[cur ^ 1] = M::lds(sb + C::DO0 + qa[c + 1]);
+            fv[cur ^ 1] = M::lds(smem + ka[c + 1] + C::KTILE);
+          }
+          s = M::mma(fq[cur], kf[c], s);
+          dp = M::mma(fd[cur], fv[cur], dp);
+          __builtin_amdgcn_sched_barrier(0);   // keep the reads one step ahead
         }
-        s = M::mma(fq[cur], kf[c], s);
-        dp = M::mma(fd[cur], fv[cur], dp);
-        __builtin_amdgcn_sched_barrier(0);   // keep the reads one step ahead
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          s = M::mma(M::lds(sb + C::Q0 + qa[c]), M::lds(smem + ka[c]), s);
+          dp = M::mma(M::lds(sb + C::DO0 + qa[c]), M::lds(smem + ka[c] + C::KTILE), dp);
+        }
       }
       // P = ex(S*factor - lse), dS = P (dP - D); masked (key > query, or a key
       // past the end) -> P = 0.
@@ -580,19 +602,27 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
       for (int t = 0; t < 32 / KC; ++t) {
         const Frag pb = M::pack(s, t);
         const Frag dsb = M::pack(dp, t);
-        Frag td[2], tqf[2];
-        td[0] = tr(C::DO0, t, 0);
-        tqf[0] = tr(C::Q0, t, 0);
+        if constexpr (KREG) {
+          Frag td[2], tqf[2];
+          td[0] = tr(C::DO0, t, 0);
+          tqf[0] = tr(C::Q0, t, 0);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int cur = db & 1;
-          if (db + 1 < NDB) {
-            td[cur ^ 1] = tr(C::DO0, t, db + 1);
-            tqf[cur ^ 1] = tr(C::Q0, t, db + 1);
+          for (int db = 0; db < NDB; ++db) {
+            const int cur = db & 1;
+            if (db + 1 < NDB) {
+              td[cur ^ 1] = tr(C::DO0, t, db + 1);
+              tqf[cur ^ 1] = tr(C::Q0, t, db + 1);
+            }
+            dv_acc[db] = M::mma(td[cur], pb, dv_acc[db]);
+            dk_acc[db] = M::mma(tqf[cur], dsb, dk_acc[db]);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          dv_acc[db] = M::mma(td[cur], pb, dv_acc[db]);
-          dk_acc[db] = M::mma(tqf[cur], dsb, dk_acc[db]);
-          __builtin_amdgcn_sched_barrier(0);
+        } else {
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            dv_acc[db] = M::mma(tr(C::DO0, t, db), pb, dv_acc[db]);
+            dk_acc[db] = M::mma(tr(C::Q0, t, db), dsb, dk_acc[db]);
+          }
         }
       }
     }
@@ -1242,7 +1272,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
                          0, stream, static_cast<const bf16*>(a.q), static_cast<const bf16*>(a.k),
                          static_cast<const bf16*>(a.v), static_cast<const bf16*>(a.dout), a.dsum, a.nlse,
                          static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), a.N, BH, n_ktiles,
-                         wg_group(n_ktiles, 32), a.scale, sp, a.drop);   // 1 workgroup per CU
+                         wg_group(n_ktiles, 32 * ((kv_two_per_cu<D, DROP>()) ? 2 : 1)), a.scale, sp,
+                         a.drop);   // 2 or 1 workgroups per CU
     } else {
       using C = BwdCfg<T, D>;
       constexpr int bytes = C::BYTES + (SPARSE ? list_bytes(kBwdListCap) : 0);
