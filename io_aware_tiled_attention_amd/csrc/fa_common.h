@@ -438,4 +438,40 @@ __device__ __forceinline__ void store4(rsrc_t r, int off, float a, float b, floa
   }
 }
 
+// Store a wave's 32 output rows, rows row0..row0+31 of a [N, D] bf16 tensor
+// (buffer `dst`), from the transposed accumulator layout: acc[db] register i
+// of lane l is element (row l % 32, column db*32 + acc_row(i, g)), times
+// `mul`.  Stored directly, every instruction would write 16-byte pieces of
+// 32 rows; instead the wave transposes the block through `buf` (its own
+// 32*D*2 bytes of idle LDS, laid out as a swizzled Tile) and writes whole
+// rows, 16 bytes per lane.  Rows past the end are dropped by the range check.
+template <int D>
+__device__ __forceinline__ void store_rows_bf16(lds_u8* buf, const f32x16 (&acc)[D / 32], float mul, rsrc_t dst,
+                                                int row0, int lane) {
+  using G = Tile<bf16, D>;
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  const int g = lane >> 5, r32 = lane & 31;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const bf16x4 x = {(bf16)(acc[db][4 * a] * mul), (bf16)(acc[db][4 * a + 1] * mul),
+                        (bf16)(acc[db][4 * a + 2] * mul), (bf16)(acc[db][4 * a + 3] * mul)};
+      *(lds_bf16x4*)(buf + G::off(r32, db * 32 + 8 * a + 4 * g)) = x;
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int LPR = G::R / 16;   // lanes per row
+  constexpr int RPI = 64 / LPR;    // rows per store
+  const int chunk = lane % LPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = lane / LPR + RPI * i;
+    const u32x4 x = *(const lds_u32x4*)(buf + row * G::R + ((chunk ^ G::swz(row)) << 4));
+    __builtin_amdgcn_raw_buffer_store_b128(x, dst, (row0 + row) * G::R + chunk * 16, 0, 0);
+  }
+}
+
 }  // namespace fa

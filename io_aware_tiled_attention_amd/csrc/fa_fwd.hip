@@ -327,14 +327,24 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   const bool no_key = !(l_tot > 0.f);
   const float inv = no_key ? 0.f : (DROP ? dp.rs : 1.f) / l_tot;
   const rsrc_t ro = make_rsrc(O + head, head_bytes);
+  if constexpr (sizeof(T) == 2 && D == 128) {
+    // Every wave has passed the loop's last barrier and no copy is in
+    // flight, so the K/V ring is idle: each wave stages its rows in a slice.
+    // (At d = 64 the round trip through LDS lengthens the epilogue of a
+    // workgroup whose LDS limits residency, and the direct stores measured
+    // faster.)
+    static_assert(kFwdWaves * kFwdQW * G::R <= L::BYTES, "O staging must fit in the K/V ring");
+    store_rows_bf16<D>(smem + w * (kFwdQW * G::R), oacc, inv, ro, qw0, lane);
+  } else {
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int d0 = db * 32 + 8 * a + 4 * g;
-      store4<T>(ro, myq * G::R + d0 * (int)sizeof(T), oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv,
-                oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv);
-    }
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = db * 32 + 8 * a + 4 * g;
+        store4<T>(ro, myq * G::R + d0 * (int)sizeof(T), oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv,
+                  oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv);
+      }
+  }
   // both lanes of a query pair write the same value
   const rsrc_t rl = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
   const float lse = no_key ? kNegInf : msub * X::kToNat + logf(l_tot);
