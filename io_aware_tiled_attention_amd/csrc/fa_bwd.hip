@@ -676,25 +676,45 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
       }
     }
   __syncthreads();
-  const rsrc_t rdk = make_rsrc(dK + head, head_bytes);
-  const rsrc_t rdv = make_rsrc(dV + head, head_bytes);
+  // Each wave adds its partner's partial, then writes its 32 rows whole
+  // through the exchange slot it has just read, which no other wave touches.
+  auto finish = [&](f32x16 (&acc)[NDB], lds_u8* x, float mul, bf16* dst) __attribute__((always_inline)) {
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int xo = ((db * 4 + a) * 64 + lane) * 16;
-      const int off = mykey * G::R + (db * 32 + 8 * a + 4 * g) * 2;
-      if (grp == 0) {
-        const f32x4 o = *(const lds_f32x4*)(xk + xo);
-        store4<bf16>(rdk, off, (dk_acc[db][4 * a] + o[0]) * scale, (dk_acc[db][4 * a + 1] + o[1]) * scale,
-                     (dk_acc[db][4 * a + 2] + o[2]) * scale, (dk_acc[db][4 * a + 3] + o[3]) * scale);
-      } else {
-        const f32x4 o = *(const lds_f32x4*)(xv + xo);
-        const float vs = DROP ? dpar.rs : 1.f;
-        store4<bf16>(rdv, off, (dv_acc[db][4 * a] + o[0]) * vs, (dv_acc[db][4 * a + 1] + o[1]) * vs,
-                     (dv_acc[db][4 * a + 2] + o[2]) * vs, (dv_acc[db][4 * a + 3] + o[3]) * vs);
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 o = *(const lds_f32x4*)(x + ((db * 4 + a) * 64 + lane) * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[db][4 * a + e] += o[e];
       }
-    }
+    store_rows_bf16<D>(x, acc, mul, make_rsrc(dst + head, head_bytes), kw0, lane);
+  };
+  static_assert(32 * G::R <= C::NACC * 64 * 4, "a wave's rows fit its exchange slot");
+  if constexpr (D == 128) {
+    if (grp == 0) finish(dk_acc, xk, scale, dK);
+    else finish(dv_acc, xv, DROP ? dpar.rs : 1.f, dV);
+  } else {
+    // d = 64 runs at 128 registers, where the staging spills: direct stores.
+    const rsrc_t rdk = make_rsrc(dK + head, head_bytes);
+    const rsrc_t rdv = make_rsrc(dV + head, head_bytes);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int xo = ((db * 4 + a) * 64 + lane) * 16;
+        const int off = mykey * G::R + (db * 32 + 8 * a + 4 * g) * 2;
+        if (grp == 0) {
+          const f32x4 o = *(const lds_f32x4*)(xk + xo);
+          store4<bf16>(rdk, off, (dk_acc[db][4 * a] + o[0]) * scale, (dk_acc[db][4 * a + 1] + o[1]) * scale,
+                       (dk_acc[db][4 * a + 2] + o[2]) * scale, (dk_acc[db][4 * a + 3] + o[3]) * scale);
+        } else {
+          const f32x4 o = *(const lds_f32x4*)(xv + xo);
+          const float vs = DROP ? dpar.rs : 1.f;
+          store4<bf16>(rdv, off, (dv_acc[db][4 * a] + o[0]) * vs, (dv_acc[db][4 * a + 1] + o[1]) * vs,
+                       (dv_acc[db][4 * a + 2] + o[2]) * vs, (dv_acc[db][4 * a + 3] + o[3]) * vs);
+        }
+      }
+  }
 }
 
 // ---------------------------------------------------------------- 3. dQ
