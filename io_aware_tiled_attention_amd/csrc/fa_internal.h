@@ -107,7 +107,8 @@ inline size_t ws_bytes(size_t rows) { return 2 * ws_dsum_bytes(rows); }
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecArgs& a, hipStream_t stream);
 hipError_t launch_forward_fp8(const Fp8Args& a, hipStream_t stream);
-// backward stages (bit mask; 7 = all): D, then dK/dV, then dQ
+// backward stages (bit mask): D, dK/dV, dQ, run in that order.  All three
+// (7) in bf16 run dQ first, with D folded into it, then dK/dV.
 constexpr int kStagePre = 1, kStageDkDv = 2, kStageDq = 4;
 hipError_t launch_backward(const BwdArgs& a, int stages, hipStream_t stream);
 

@@ -10,10 +10,12 @@
 // hipGetSymbolAddress (host code must never pass the array's own name to a
 // kernel: on the host that name is a stand-in, not a device address) and
 // kept per device; the kernels receive that address exactly as they receive
-// a caller's workspace.  Nothing is cleared: the preprocess kernel writes
-// every statistic the later kernels read, on the same stream, before they
-// run.  All calls on one GPU share its array, so calls that overlap in time
-// on one GPU (different streams, or host threads) race on it.
+// a caller's workspace.  Nothing is cleared: the backward's first kernel
+// (bf16: dQ, which also does the preprocess pass; fp32: the preprocess
+// kernel) writes every statistic the later kernels read, on the same
+// stream, before they run.  All calls on one GPU share its array, so calls
+// that overlap in time on one GPU (different streams, or host threads) race
+// on it.
 #include "fa.h"
 #include "fa_internal.h"
 
