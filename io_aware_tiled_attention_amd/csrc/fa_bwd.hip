@@ -152,7 +152,7 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
   Frag kf[D / KC], vf[D / KC];
 #pragma unroll
   for (int c = 0; c < D / KC; ++c) {
-    const int off = mykey * G::R + (c * KC + g * KPL) * (int)sizeof(T);
+    const uint32_t off = (uint32_t)mykey * G::R + (c * KC + g * KPL) * (int)sizeof(T);
     kf[c] = M::load(rk, off);
     vf[c] = M::load(rv, off);
   }
@@ -329,7 +329,7 @@ void fa_bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const 
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int off = mykey * G::R + (db * 32 + 8 * a + 4 * g) * (int)sizeof(T);
+      const uint32_t off = (uint32_t)mykey * G::R + (db * 32 + 8 * a + 4 * g) * (int)sizeof(T);
       store4<T>(rdk, off, dk_acc[db][4 * a] * scale, dk_acc[db][4 * a + 1] * scale, dk_acc[db][4 * a + 2] * scale,
                 dk_acc[db][4 * a + 3] * scale);
       const float vs = DROP ? dpar.rs : 1.f;
@@ -702,7 +702,7 @@ void fa_bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int xo = ((db * 4 + a) * 64 + lane) * 16;
-        const int off = mykey * G::R + (db * 32 + 8 * a + 4 * g) * 2;
+        const uint32_t off = (uint32_t)mykey * G::R + (db * 32 + 8 * a + 4 * g) * 2;
         if (grp == 0) {
           const f32x4 o = *(const lds_f32x4*)(xk + xo);
           store4<bf16>(rdk, off, (dk_acc[db][4 * a] + o[0]) * scale, (dk_acc[db][4 * a + 1] + o[1]) * scale,
@@ -773,7 +773,7 @@ void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
   Frag qf[D / KC], dof[D / KC];
 #pragma unroll
   for (int c = 0; c < D / KC; ++c) {
-    const int off = myq * G::R + (c * KC + g * KPL) * (int)sizeof(T);
+    const uint32_t off = (uint32_t)myq * G::R + (c * KC + g * KPL) * (int)sizeof(T);
     qf[c] = M::load(rq, off);
     dof[c] = M::load(rdo, off);
   }
@@ -908,7 +908,7 @@ void fa_bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int a = 0; a < 4; ++a)
-      store4<T>(rdq, myq * G::R + (db * 32 + 8 * a + 4 * g) * (int)sizeof(T), acc[db][4 * a] * scale,
+      store4<T>(rdq, (uint32_t)myq * G::R + (db * 32 + 8 * a + 4 * g) * (int)sizeof(T), acc[db][4 * a] * scale,
                 acc[db][4 * a + 1] * scale, acc[db][4 * a + 2] * scale, acc[db][4 * a + 3] * scale);
 }
 
@@ -979,7 +979,7 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   Frag qf[NC], dof[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int off = myq * G::R + (c * KC + g * KPL) * 2;
+    const uint32_t off = (uint32_t)myq * G::R + (c * KC + g * KPL) * 2;
     qf[c] = M::load(rq, off);
     dof[c] = M::load(rdo, off);
   }
@@ -993,7 +993,7 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
     float part[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const Frag of = M::load(ro, myq * G::R + (c * KC + g * KPL) * 2);
+      const Frag of = M::load(ro, (uint32_t)myq * G::R + (c * KC + g * KPL) * 2);
       float acc = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc += (float)of[e] * (float)dof[c][e];
@@ -1251,7 +1251,7 @@ void fa_bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int a = 0; a < 4; ++a)
-      store4<bf16>(rdq, myq * G::R + (db * 32 + 8 * a + 4 * g) * 2, acc[db][4 * a] * scale,
+      store4<bf16>(rdq, (uint32_t)myq * G::R + (db * 32 + 8 * a + 4 * g) * 2, acc[db][4 * a] * scale,
                    acc[db][4 * a + 1] * scale, acc[db][4 * a + 2] * scale, acc[db][4 * a + 3] * scale);
 }
 

@@ -169,7 +169,7 @@ __device__ __forceinline__ void tile_to_lds(rsrc_t src, lds_u8* tile, int row0, 
     const int o = s * 1024 + lane * 16;
     const int row = o / G::R;
     const int chunk = ((o % G::R) >> 4) ^ G::swz(row);
-    lds_dma16(src, tile + s * 1024, (row0 + row) * G::R + chunk * 16);
+    lds_dma16(src, tile + s * 1024, (uint32_t)(row0 + row) * G::R + chunk * 16);
   }
 }
 
@@ -186,8 +186,8 @@ __device__ __forceinline__ void tile_to_lds_async(u32x4 src, lds_u8* tile, int r
     const int o = s * 1024 + lane * 16;
     const int row = o / G::R;
     const int chunk = ((o % G::R) >> 4) ^ G::swz(row);
-    if constexpr (STREAM) lds_dma16_async_nt(src, tile + s * 1024, (row0 + row) * G::R + chunk * 16);
-    else lds_dma16_async(src, tile + s * 1024, (row0 + row) * G::R + chunk * 16);
+    if constexpr (STREAM) lds_dma16_async_nt(src, tile + s * 1024, (uint32_t)(row0 + row) * G::R + chunk * 16);
+    else lds_dma16_async(src, tile + s * 1024, (uint32_t)(row0 + row) * G::R + chunk * 16);
   }
 }
 
@@ -470,7 +470,7 @@ __device__ __forceinline__ void store_rows_bf16(lds_u8* buf, const f32x16 (&acc)
   for (int i = 0; i < 32 / RPI; ++i) {
     const int row = lane / LPR + RPI * i;
     const u32x4 x = *(const lds_u32x4*)(buf + row * G::R + ((chunk ^ G::swz(row)) << 4));
-    __builtin_amdgcn_raw_buffer_store_b128(x, dst, (row0 + row) * G::R + chunk * 16, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(x, dst, (uint32_t)(row0 + row) * G::R + chunk * 16, 0, 0);
   }
 }
 

@@ -139,7 +139,7 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   // Q^T as the B operand of S^T = K Q^T: column = query, KPL d-values of group g.
   Frag qf[D / KC];
 #pragma unroll
-  for (int c = 0; c < D / KC; ++c) qf[c] = M::load(rq, myq * G::R + (c * KC + g * KPL) * (int)sizeof(T));
+  for (int c = 0; c < D / KC; ++c) qf[c] = M::load(rq, (uint32_t)myq * G::R + (c * KC + g * KPL) * (int)sizeof(T));
 
   const int kv_end = CAUSAL ? min(N, q0 + kFwdBR) : N;
   const int ntiles = (kv_end + kFwdBC - 1) / kFwdBC;
@@ -341,7 +341,7 @@ void fa_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int d0 = db * 32 + 8 * a + 4 * g;
-        store4<T>(ro, myq * G::R + d0 * (int)sizeof(T), oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv,
+        store4<T>(ro, (uint32_t)myq * G::R + d0 * (int)sizeof(T), oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv,
                   oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv);
       }
   }

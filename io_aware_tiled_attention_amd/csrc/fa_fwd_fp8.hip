@@ -83,7 +83,7 @@ __device__ __forceinline__ void tile8_to_lds(rsrc_t src, lds_u8* tile, int row0,
     const int o = s * 1024 + lane * 16;
     const int row = o / G::R;
     const int chunk = ((o % G::R) >> 4) ^ G::swz(row);
-    lds_dma16(src, tile + s * 1024, (row0 + row) * G::R + chunk * 16);
+    lds_dma16(src, tile + s * 1024, (uint32_t)(row0 + row) * G::R + chunk * 16);
   }
 }
 
@@ -141,9 +141,9 @@ void fa_fwd_fp8_kernel(const unsigned char* __restrict__ Q, const unsigned char*
   i32x8 qf[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, myq * G::R + 64 * c + 32 * g, 0, 0));
-    const u32x4 hi =
-        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, myq * G::R + 64 * c + 32 * g + 16, 0, 0));
+    const uint32_t qo = (uint32_t)myq * G::R + 64 * c + 32 * g;
+    const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qo, 0, 0));
+    const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qo + 16, 0, 0));
     qf[c] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   }
   // Per-lane LDS offsets, the same for every tile (the swizzle is periodic in 32 rows):
